@@ -1,0 +1,187 @@
+"""Thin ctypes binding over libfa.so (include/fa.h): argument marshalling only.
+
+Every step of the attention computation runs in the library's HIP kernels.
+PyTorch supplies device memory (tensors) and the stream; nothing here computes.
+If libfa.so is missing the binding raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_WORKSPACE = 3
+FA_ERR_HIP = 4
+FA_BWD_5GEMM_ATOMIC = 0
+FA_BWD_7GEMM = 1
+PASS_FWD, PASS_DKDV, PASS_DKDV_ATOMIC, PASS_DQ = 0, 1, 2, 3
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s" % (what, fa_status_string(status)))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libfa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfa.so is not built (%s); run __graft_entry__.build() or "
+                           "python -m exact_attention_102_amd.build" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz, cp = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_char_p
+    L.fa_fwd.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, vp, vp]
+    L.fa_fwd.restype = i
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i]
+    L.fa_fwd_ex.restype = i
+    L.fa_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp]
+    L.fa_bwd.restype = i
+    L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp, i, i]
+    L.fa_bwd_ex.restype = i
+    L.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, vp, i, vp]
+    L.fa_bwd_preprocess.restype = i
+    L.fa_num_configs.argtypes = [i, i, i]
+    L.fa_num_configs.restype = i
+    L.fa_config_name.argtypes = [i, i, i, i, cp, sz]
+    L.fa_config_name.restype = i
+    L.fa_default_config.argtypes = [i, i, i]
+    L.fa_default_config.restype = i
+    L.fa_status_string.argtypes = [i]
+    L.fa_status_string.restype = cp
+    L.fa_version.argtypes = []
+    L.fa_version.restype = cp
+    _lib = L
+    return L
+
+
+def fa_status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def fa_version() -> str:
+    return lib().fa_version().decode()
+
+
+def fa_num_configs(pass_id: int, d: int, causal: bool = False) -> int:
+    return lib().fa_num_configs(int(pass_id), int(d), int(bool(causal)))
+
+
+def fa_config_name(pass_id: int, d: int, causal: bool, index: int) -> str:
+    buf = ctypes.create_string_buffer(128)
+    if lib().fa_config_name(int(pass_id), int(d), int(bool(causal)), int(index), buf, 128) != 0:
+        raise IndexError("no configuration %d for pass %d, d=%d" % (index, pass_id, d))
+    return buf.value.decode()
+
+
+def fa_default_config(pass_id: int, d: int, causal: bool = False) -> int:
+    return lib().fa_default_config(int(pass_id), int(d), int(bool(causal)))
+
+
+def fa_bwd_workspace_size(B: int, H: int, N: int, d: int, variant: int = FA_BWD_7GEMM) -> int:
+    return int(lib().fa_bwd_workspace_size(int(B), int(H), int(N), int(d), int(variant)))
+
+
+# --------------------------------------------------------------------------- torch marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(stream.cuda_stream))
+
+
+def _check(t, name, dtype, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device (cuda/HIP) tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous [B, H, N, d]" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, cfg: int = -1):
+    """Forward: returns (o fp32 [B,H,N,d], lse fp32 [B,H,N]); allocates outputs if not given."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    pq = _check(q, "q", torch.bfloat16)
+    pk = _check(k, "k", torch.bfloat16, q.shape)
+    pv = _check(v, "v", torch.bfloat16, q.shape)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    po = _check(o, "o", torch.float32, q.shape)
+    pl = _check(lse, "lse", torch.float32, (B, H, N))
+    st = lib().fa_fwd_ex(pq, pk, pv, B, H, N, d, int(bool(causal)), float(scale), po, pl, _stream_ptr(stream), int(cfg))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
+           dq=None, dk=None, dv=None, workspace=None, stream=None, cfg_dkdv: int = -1, cfg_dq: int = -1):
+    """Backward: returns (dq, dk, dv), fp32 [B,H,N,d]; allocates outputs/workspace if not given."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    ptr = [_check(q, "q", torch.bfloat16), _check(k, "k", torch.bfloat16, q.shape),
+           _check(v, "v", torch.bfloat16, q.shape), _check(o, "o", torch.float32, q.shape),
+           _check(lse, "lse", torch.float32, (B, H, N)), _check(dout, "dout", torch.bfloat16, q.shape)]
+    outs = []
+    for t, name in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        if t is None:
+            t = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        outs.append(t)
+    pouts = [_check(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
+    need = fa_bwd_workspace_size(B, H, N, d, variant)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fa_bwd_ex(*ptr, B, H, N, d, int(bool(causal)), float(scale), int(variant), *pouts,
+                         ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream_ptr(stream), int(cfg_dkdv), int(cfg_dq))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return tuple(outs)
+
+
+def fa_bwd_preprocess(o, dout, delta=None, dq=None, stream=None):
+    """delta[b,h,i] = sum_k dout * o (and zeroes dq when given); returns delta."""
+    torch = _torch()
+    B, H, N, d = o.shape
+    po = _check(o, "o", torch.float32)
+    pd = _check(dout, "dout", torch.bfloat16, o.shape)
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    pdel = _check(delta, "delta", torch.float32, (B, H, N))
+    pdq = _check(dq, "dq", torch.float32, o.shape) if dq is not None else ctypes.c_void_p(0)
+    st = lib().fa_bwd_preprocess(po, pd, B, H, N, d, pdel, pdq, int(dq is not None), _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_preprocess")
+    return delta

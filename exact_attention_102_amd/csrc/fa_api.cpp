@@ -1,0 +1,295 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation, tile
+// configuration selection and kernel dispatch.  Nothing here allocates, frees or
+// synchronises; every launch goes onto the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+using fa::BwdConfig;
+using fa::FwdConfig;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  const char* lo;
+  size_t bytes;
+};
+
+bool overlaps(Range a, Range b) {
+  if (!a.lo || !b.lo || a.bytes == 0 || b.bytes == 0) return false;
+  return a.lo < b.lo + b.bytes && b.lo < a.lo + a.bytes;
+}
+
+Range rng(const void* p, size_t bytes) { return Range{static_cast<const char*>(p), bytes}; }
+
+bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Shared size checks: positive sizes, 32-bit grid and row counts, 64-bit byte counts.
+fa_status check_sizes(int B, int H, int N, int d, float scale) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * H * N;
+  if (rows > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+const FwdConfig* fwd_table(int* n) { return fa::fwd_configs(n); }
+
+const BwdConfig* bwd_table(int pass, int* n) {
+  switch (pass) {
+    case 1: return fa::dkdv_configs(n);
+    case 2: return fa::dkdv_atomic_configs(n);
+    case 3: return fa::dq_configs(n);
+    default: *n = 0; return nullptr;
+  }
+}
+
+// Index of the i-th configuration of `pass` with head dim d, or -1.
+template <class Cfg>
+int nth_for_d(const Cfg* t, int n, int d, int i) {
+  int seen = 0;
+  for (int j = 0; j < n; ++j) {
+    if (t[j].d != d) continue;
+    if (seen == i) return j;
+    ++seen;
+  }
+  return -1;
+}
+
+template <class Cfg>
+int count_for_d(const Cfg* t, int n, int d) {
+  int c = 0;
+  for (int j = 0; j < n; ++j) c += (t[j].d == d);
+  return c;
+}
+
+// Default configuration per (pass, d, causal), as chosen by the block-shape sweep;
+// expressed as an index among the pass's configurations for that d.
+int default_index(int pass, int d, int causal) {
+  (void)causal;
+  switch (pass) {
+    case 0: return d == 64 ? 0 : d == 128 ? 0 : 0;
+    case 1: return 0;
+    case 2: return 0;
+    case 3: return d == 64 ? 0 : d == 128 ? 0 : 0;
+    default: return -1;
+  }
+}
+
+fa_status launched() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    std::fprintf(stderr, "fa: kernel launch failed: %s\n", hipGetErrorString(e));
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument (null/misaligned pointer, size, scale or aliasing)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head dimension, variant or configuration";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch error";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_version(void) { return "fa-mi355x 0.1 gfx950"; }
+
+int fa_num_configs(int pass, int d, int causal) {
+  (void)causal;
+  int n = 0;
+  if (pass == 0) {
+    const FwdConfig* t = fwd_table(&n);
+    return count_for_d(t, n, d);
+  }
+  const BwdConfig* t = bwd_table(pass, &n);
+  return t ? count_for_d(t, n, d) : 0;
+}
+
+int fa_config_name(int pass, int d, int causal, int index, char* buf, size_t buf_len) {
+  (void)causal;
+  if (!buf || buf_len == 0) return -1;
+  int n = 0;
+  const char* name = nullptr;
+  if (pass == 0) {
+    const FwdConfig* t = fwd_table(&n);
+    const int j = nth_for_d(t, n, d, index);
+    if (j >= 0) name = t[j].name;
+  } else {
+    const BwdConfig* t = bwd_table(pass, &n);
+    const int j = t ? nth_for_d(t, n, d, index) : -1;
+    if (j >= 0) name = t[j].name;
+  }
+  if (!name) return -1;
+  std::snprintf(buf, buf_len, "%s", name);
+  return 0;
+}
+
+int fa_default_config(int pass, int d, int causal) {
+  if (!supported_d(d)) return -1;
+  return default_index(pass, d, causal);
+}
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                    float scale, float* o, float* lse, void* stream, int cfg) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_sizes(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  const size_t elems = (size_t)B * H * N * d;
+  const Range in[3] = {rng(q, elems * 2), rng(k, elems * 2), rng(v, elems * 2)};
+  const Range ro = rng(o, elems * 4), rl = rng(lse, (size_t)B * H * N * 4);
+  for (const Range& r : in)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_INVALID_ARG;
+  if (overlaps(ro, rl)) return FA_ERR_INVALID_ARG;
+
+  int n = 0;
+  const FwdConfig* t = fwd_table(&n);
+  const int idx = cfg < 0 ? default_index(0, d, causal) : cfg;
+  const int j = nth_for_d(t, n, d, idx);
+  if (j < 0) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                 float scale, float* o, float* lse, void* stream) {
+  return fa_fwd_ex(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_bwd_variant variant) {
+  if (check_sizes(B, H, N, d, 1.0f) != FA_OK) return 0;
+  if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int N, int d, float* delta, float* dq,
+                            int zero_dq, void* stream) {
+  if (!o || !dout || !delta || (zero_dq && !dq)) return FA_ERR_INVALID_ARG;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(delta) || (zero_dq && !aligned16(dq))) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_sizes(B, H, N, d, 1.0f);
+  if (sz != FA_OK) return sz;
+  const size_t elems = (size_t)B * H * N * d;
+  const Range rd = rng(delta, (size_t)B * H * N * 4);
+  const Range rq = zero_dq ? rng(dq, elems * 4) : Range{nullptr, 0};
+  if (overlaps(rd, rng(o, elems * 4)) || overlaps(rd, rng(dout, elems * 2)) || overlaps(rq, rng(o, elems * 4)) ||
+      overlaps(rq, rng(dout, elems * 2)) || overlaps(rq, rd))
+    return FA_ERR_INVALID_ARG;
+  fa::PreArgs p;
+  p.o = o;
+  p.dout = static_cast<const __bf16*>(dout);
+  p.delta = delta;
+  p.dq = zero_dq ? dq : nullptr;
+  p.rows = B * H * N;
+  if (fa::launch_preprocess(p, d, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_UNSUPPORTED;
+  return launched();
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                    int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                    float* dv, void* workspace, size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_sizes(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return FA_ERR_UNSUPPORTED;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, variant);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t rows = (size_t)B * H * N;
+  const Range ins[] = {rng(q, elems * 2), rng(k, elems * 2),   rng(v, elems * 2),
+                       rng(o, elems * 4), rng(lse, rows * 4), rng(dout, elems * 2)};
+  const Range outs[] = {rng(dq, elems * 4), rng(dk, elems * 4), rng(dv, elems * 4), rng(workspace, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+  }
+
+  const bool atomic = variant == FA_BWD_5GEMM_ATOMIC;
+  int n1 = 0, n3 = 0;
+  const BwdConfig* t1 = bwd_table(atomic ? 2 : 1, &n1);
+  const int i1 = nth_for_d(t1, n1, d, cfg_dkdv < 0 ? default_index(atomic ? 2 : 1, d, causal) : cfg_dkdv);
+  if (i1 < 0) return FA_ERR_UNSUPPORTED;
+  const BwdConfig* t3 = bwd_table(3, &n3);
+  int i3 = -1;
+  if (!atomic) {
+    i3 = nth_for_d(t3, n3, d, cfg_dq < 0 ? default_index(3, d, causal) : cfg_dq);
+    if (i3 < 0) return FA_ERR_UNSUPPORTED;
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  fa::PreArgs p;
+  p.o = o;
+  p.dout = static_cast<const __bf16*>(dout);
+  p.delta = delta;
+  p.dq = atomic ? dq : nullptr;
+  p.rows = (int)rows;
+  if (fa::launch_preprocess(p, d, s) != 0) return FA_ERR_UNSUPPORTED;
+  fa_status st = launched();
+  if (st != FA_OK) return st;
+
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
+  st = launched();
+  if (st != FA_OK || atomic) return st;
+  if (t3[i3].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                 int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                 float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace,
+                   workspace_bytes, stream, -1, -1);
+}
+
+}  // extern "C"

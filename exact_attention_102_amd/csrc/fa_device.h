@@ -1,0 +1,163 @@
+// fa_device.h -- device-side building blocks shared by the forward and backward
+// kernels for gfx950 (CDNA4): MFMA wrappers, the swizzled LDS tile layout with
+// its row-fragment and transposed (column) fragment reads, cross-half row
+// reductions, and the work-item mapping over the 8 XCDs.
+//
+// MFMA register layouts (v_mfma_f32_32x32x16_bf16, one wave64):
+//   A (32 x 16): lane l holds A[l % 32][8 * (l / 32) + e], e = 0..7
+//   B (16 x 32): lane l holds B[8 * (l / 32) + e][l % 32]
+//   C (32 x 32): lane l, register r holds C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]
+// Row-fragment reads (ds_read_b128) feed operands whose contraction index runs
+// along a tile row (d for Q K^T); column-fragment reads (two ds_read_b64_tr_b16)
+// feed operands whose contraction index runs down a tile column (the key index of
+// V in P V, the query index of Q and dO in dS^T Q and P^T dO).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define LDS __attribute__((address_space(3)))
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+namespace fa {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// The C layout puts rows 8a + 4b + i (b = lane half) in register 4a + i.  Feeding
+// an MFMA's A operand row R with tile row pi(R) makes lane half g, registers
+// 8h + e hold tile rows 16h + 8g + e: eight consecutive rows per register octet,
+// exactly the k-slice a following MFMA's B operand wants for lane half g.
+__device__ __forceinline__ int pi_row(int R) {
+  const int a = R >> 3, b = (R >> 2) & 1, i = R & 3;
+  return ((a >> 1) << 4) + (b << 3) + ((a & 1) << 2) + i;
+}
+
+// ---------------------------------------------------------------------------
+// Swizzled LDS tile of bf16, W elements per row (row pitch 2W bytes, no padding).
+// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r).  The XOR
+// pattern keeps both access shapes free of bank conflicts on a 64-bank LDS:
+//  * row fragments: 16 lanes read the same chunk of 16 distinct rows;
+//  * transposed reads: 32 lanes read 4 consecutive rows x 64 contiguous bytes;
+//  * staging writes: 16 lanes write 256 contiguous bytes.
+template <int W>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (W == 32) {
+    return (row >> 2) & 3;
+  } else if constexpr (W == 64) {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | (x >> 1);
+  } else {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ int tile_off(int row, int col) {  // byte offset of element (row, col)
+  return row * (2 * W) + ((((col >> 3) ^ swz<W>(row))) << 4) + ((col & 7) << 1);
+}
+
+// 8 consecutive elements of one row (col multiple of 8).
+template <int W>
+__device__ __forceinline__ bf16x8 row_frag(const LDS char* tile, int row, int col) {
+  return *(const LDS bf16x8*)(tile + tile_off<W>(row, col));
+}
+
+// Operand with the contraction index running down the tile's rows: lane l gets
+// tile[r0 + 8 * (l / 32) + e][c0 + l % 32], e = 0..7.  Each ds_read_b64_tr_b16
+// takes, per group of 16 lanes, four row segments of 4 elements and hands lane i
+// the four values of column i; lane j of the group supplies row j / 4, columns
+// 4 * (j % 4) .. +3.
+template <int W>
+__device__ __forceinline__ bf16x8 col_frag(const LDS char* tile, int r0, int c0, int lane) {
+  const int row = r0 + ((lane >> 5) << 3) + ((lane & 15) >> 2);
+  const int col = c0 + (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(tile + tile_off<W>(row, col)));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(tile + tile_off<W>(row + 4, col)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Register-staged copy of a ROWS x W bf16 tile from global memory (rows of pitch
+// W elements, rows >= valid_rows read as zeros) into the swizzled LDS layout.
+// NT threads cooperate; each moves ROWS * W / 8 / NT chunks of 16 bytes.
+template <int ROWS, int W, int NT>
+struct TileStager {
+  static constexpr int kChunks = ROWS * W / 8;
+  static constexpr int kPer = kChunks / NT;
+  static_assert(kChunks % NT == 0, "tile chunks must divide evenly over the threads");
+  u32x4 reg[kPer];
+
+  __device__ __forceinline__ void load(const __bf16* g, int row0, int valid_rows, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / (W / 8), c = idx % (W / 8);
+      if (row0 + r < valid_rows) {
+        reg[i] = *(const u32x4*)(g + (size_t)(row0 + r) * W + c * 8);
+      } else {
+        reg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(LDS char* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int idx = tid + i * NT;
+      const int r = idx / (W / 8), c = idx % (W / 8);
+      *(LDS u32x4*)(tile + tile_off<W>(r, c * 8)) = reg[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Reductions across the two 32-lane halves (lane l and lane l ^ 32), which hold
+// the two halves of a 32-key (or 32-query) block in the C layout.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)p[0]), __builtin_bit_cast(float, (unsigned)p[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)v[base + e];
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Work-item mapping.  Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup x lands on XCD x % 8), each with its own L2.  Remapping so that
+// every XCD walks a contiguous range of work items keeps the tiles of one
+// (batch, head) -- which all re-read the same K/V or Q/dO -- in one L2.
+__device__ __forceinline__ int xcd_remap(int x, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int xcd = x & 7, local = x >> 3;
+  return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+}  // namespace fa

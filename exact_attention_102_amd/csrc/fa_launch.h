@@ -1,0 +1,68 @@
+// fa_launch.h -- host/device argument blocks and the per-pass tile-configuration
+// tables that the C ABI (fa_api.cpp) dispatches through.
+#pragma once
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  float* o;
+  float* lse;
+  int B, H, N;
+  float scale;
+};
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  int B, H, N;
+  float scale;
+};
+
+struct PreArgs {
+  const float* o;
+  const __bf16* dout;
+  float* delta;
+  float* dq;  // zeroed when non-null
+  int rows;   // B * H * N
+};
+
+typedef int (*FwdLaunch)(const FwdArgs&, bool causal, hipStream_t);
+typedef int (*BwdLaunch)(const BwdArgs&, bool causal, hipStream_t);
+
+struct FwdConfig {
+  int d;
+  int rows;   // query rows per workgroup
+  int cols;   // keys per LDS tile
+  int waves;
+  const char* name;
+  FwdLaunch launch;
+};
+
+struct BwdConfig {
+  int d;
+  int rows;   // rows owned per workgroup (keys for dK/dV, queries for dQ)
+  int cols;   // rows per LDS tile along the traversal
+  int waves;
+  const char* name;
+  BwdLaunch launch;
+};
+
+const FwdConfig* fwd_configs(int* count);
+const BwdConfig* dkdv_configs(int* count);         // 7-GEMM dK/dV (no dQ)
+const BwdConfig* dkdv_atomic_configs(int* count);  // 5-GEMM dK/dV with fp32-atomic dQ
+const BwdConfig* dq_configs(int* count);           // 7-GEMM dQ
+
+int launch_preprocess(const PreArgs& a, int d, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,135 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) fused exact-attention library (libfa.so).
+ *
+ * The operation is exact scaled-dot-product attention, O = softmax(scale * Q K^T) V,
+ * computed as a tiled, IO-aware fused kernel: the N x N score matrix never reaches
+ * HBM; the forward keeps a running row maximum m and a running sum of exponentials l
+ * per query row and saves only O and the log-sum-exp ("ELI5: FlashAttention",
+ * highlights on kernel fusion, tiling and the m(x)/l(x) statistics).  The backward
+ * recomputes S and P from Q, K and the log-sum-exp ("ELI5: FlashAttention",
+ * recomputation highlight) in one of the two designs compared in "Potential
+ * algorithmic improvements for backward pass" (flash-attention issue 1172):
+ *   - FA_BWD_5GEMM_ATOMIC: one dK/dV kernel that also accumulates dQ with fp32
+ *     atomics (S, dP, dV, dK, dQ: five GEMMs; non-deterministic summation order);
+ *   - FA_BWD_7GEMM: a dK/dV kernel (four GEMMs) followed by a separate dQ kernel
+ *     that walks the keys in the forward's direction (three GEMMs); no atomics, so
+ *     results are bitwise reproducible.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  Layout     every tensor is contiguous [B, H, N, d] (d fastest), the statistics
+ *             lse / delta are contiguous [B, H, N].  N_q == N_k == N.
+ *  dtypes     q, k, v, dout: bfloat16 (raw 16-bit storage, passed as void*);
+ *             o, lse, dq, dk, dv, delta: float32.
+ *  Math       scale multiplies Q K^T; causal means query i attends to keys j <= i;
+ *             lse is the natural-log log-sum-exp of the scaled, masked scores.
+ *  Memory     every pointer is device memory allocated and owned by the caller; the
+ *             library never allocates, frees or synchronises.  Pointers must be
+ *             16-byte aligned.  Outputs may not alias inputs.
+ *  Stream     all work is enqueued on `stream` (a hipStream_t; NULL = the legacy
+ *             default stream) and is asynchronous: kernel faults surface at the
+ *             caller's next synchronisation.
+ *  Errors     arguments are validated before anything is enqueued; on any error
+ *             nothing is launched and outputs are untouched.  FA_ERR_INVALID_ARG:
+ *             null/misaligned pointer, B, H or N <= 0, non-finite or non-positive
+ *             scale, aliasing, or a tensor too large for 32-bit in-head indexing;
+ *             FA_ERR_UNSUPPORTED: head dim not in {64, 128, 256} or unknown
+ *             variant/config; FA_ERR_WORKSPACE: workspace missing or too small;
+ *             FA_ERR_HIP: a launch failed (hipGetLastError after the launch).
+ *  Threads    stateless apart from a once-initialised device-property cache;
+ *             safe to call from several host threads.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_WORKSPACE = 3,
+  FA_ERR_HIP = 4
+} fa_status;
+
+typedef enum {
+  FA_BWD_5GEMM_ATOMIC = 0, /* dK/dV kernel with fused fp32-atomic dQ (5 GEMMs)          */
+  FA_BWD_7GEMM = 1         /* dK/dV kernel, then a separate forward-direction dQ kernel */
+} fa_bwd_variant;
+
+/* Forward pass.
+ * Computes o = softmax(scale * q k^T, causal mask) v and lse (natural log) per
+ * query row ("ELI5: FlashAttention": tiling plus the online m/l statistics;
+ * issue 1172, opening comment: the log-sum-exp is the saved operand).
+ *   q, k, v : bf16 [B,H,N,d]          (read)
+ *   o       : fp32 [B,H,N,d]          (written)
+ *   lse     : fp32 [B,H,N]            (written)
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                 float scale, float* o, float* lse, void* stream);
+
+/* Bytes of workspace fa_bwd needs: the fp32 row term delta_i = sum_k dO_ik O_ik,
+ * [B,H,N] floats, for either variant.  Returns 0 for invalid sizes. */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, fa_bwd_variant variant);
+
+/* Backward pass: gradients of L = sum(dout * o) with respect to q, k, v.
+ * Recomputes S and P from q, k and lse (issue 1172: recomputation instead of
+ * storing P; "ELI5: FlashAttention", recomputation highlight), in the chosen
+ * design (see the top of this file).  causal and scale must equal the forward's.
+ *   q, k, v, dout : bf16 [B,H,N,d]    (read)
+ *   o, lse        : fp32, as written by fa_fwd (read)
+ *   dq, dk, dv    : fp32 [B,H,N,d]    (written; dq is zeroed by the library first
+ *                                      for the atomic variant)
+ *   workspace     : >= fa_bwd_workspace_size bytes of device memory, 16-B aligned
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                 const void* dout, int B, int H, int N, int d, int causal, float scale,
+                 fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* The backward's first step on its own: delta_i = sum_k dout_ik * o_ik per row
+ * (the softmax-backward row term, computed from O instead of from P and dP; the
+ * two are equal because O = P V and dP = dO V^T).  When zero_dq is non-zero it
+ * also writes zeros to dq (the atomic variant's accumulator).
+ *   o : fp32 [B,H,N,d], dout : bf16 [B,H,N,d], delta : fp32 [B,H,N], dq : fp32 or NULL */
+fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int N, int d, float* delta,
+                            float* dq, int zero_dq, void* stream);
+
+/* Tile configurations, for the block-shape sweep ("Potential algorithmic
+ * improvements for backward pass": search over block dimensions under register
+ * pressure; non-square blocks such as 32-64 x 160-320).
+ * pass: 0 = forward, 1 = backward dK/dV (7-GEMM), 2 = backward dK/dV with atomic dQ,
+ *       3 = backward dQ (7-GEMM).
+ * fa_num_configs returns how many configurations exist for (pass, d, causal);
+ * fa_config_name writes a NUL-terminated description of config `index` into buf
+ * (rows per workgroup x keys/queries per tile, waves) and returns 0, or -1 if out
+ * of range.  fa_default_config returns the index the plain entry points use. */
+int fa_num_configs(int pass, int d, int causal);
+int fa_config_name(int pass, int d, int causal, int index, char* buf, size_t buf_len);
+int fa_default_config(int pass, int d, int causal);
+
+/* fa_fwd / fa_bwd with explicit tile configurations (-1 = default).  For fa_bwd_ex,
+ * cfg_dkdv indexes pass 1 or 2 according to the variant, cfg_dq indexes pass 3
+ * (ignored by the atomic variant). */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                    float scale, float* o, float* lse, void* stream, int cfg);
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                    const void* dout, int B, int H, int N, int d, int causal, float scale,
+                    fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
+                    size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_string(fa_status s);
+
+/* Library version string, e.g. "fa-mi355x 0.1 gfx950". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

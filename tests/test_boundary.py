@@ -1,0 +1,160 @@
+"""CPU tests of the C ABI boundary: the library loads, exports every entry point
+include/fa.h declares, and rejects invalid arguments before launching anything.
+No test here reaches a kernel launch (there is no GPU on this host)."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from exact_attention_102_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from exact_attention_102_amd import build
+        build.build()
+    return binding.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), "libfa.so does not export " + n
+
+
+def test_status_strings_and_version(L):
+    from exact_attention_102_amd import fa_status_string, fa_version
+    assert fa_status_string(0) == "FA_OK"
+    for s in range(1, 5):
+        assert fa_status_string(s).startswith("FA_ERR_")
+    assert "gfx950" in fa_version()
+
+
+def test_config_tables(L):
+    from exact_attention_102_amd import fa_config_name, fa_default_config, fa_num_configs
+    for p in range(4):
+        for d in (64, 128, 256):
+            n = fa_num_configs(p, d)
+            assert n >= 1
+            names = [fa_config_name(p, d, False, i) for i in range(n)]
+            assert all(("d%d" % d) in s for s in names)
+            assert 0 <= fa_default_config(p, d) < n
+            with pytest.raises(IndexError):
+                fa_config_name(p, d, False, n)
+        assert fa_num_configs(p, 96) == 0
+        assert fa_default_config(p, 96) == -1
+
+
+P = 0x7f0000000000            # fake, 16-byte aligned, never dereferenced (validation fails first)
+MB = 1 << 20
+
+
+def fwd(L, q=P, k=P + 64 * MB, v=P + 128 * MB, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+        o=P + 192 * MB, lse=P + 256 * MB):
+    return L.fa_fwd(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), B, H, N, d, causal, scale,
+                    ctypes.c_void_p(o), ctypes.c_void_p(lse), None)
+
+
+def test_fwd_rejects_bad_arguments(L):
+    from exact_attention_102_amd import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED
+    assert fwd(L, q=0) == FA_ERR_INVALID_ARG
+    assert fwd(L, o=0) == FA_ERR_INVALID_ARG
+    assert fwd(L, lse=0) == FA_ERR_INVALID_ARG
+    assert fwd(L, q=P + 8) == FA_ERR_INVALID_ARG          # misaligned
+    assert fwd(L, B=0) == FA_ERR_INVALID_ARG
+    assert fwd(L, H=-1) == FA_ERR_INVALID_ARG
+    assert fwd(L, N=0) == FA_ERR_INVALID_ARG
+    assert fwd(L, d=96) == FA_ERR_UNSUPPORTED
+    assert fwd(L, d=0) == FA_ERR_UNSUPPORTED
+    assert fwd(L, scale=0.0) == FA_ERR_INVALID_ARG
+    assert fwd(L, scale=-1.0) == FA_ERR_INVALID_ARG
+    assert fwd(L, scale=float("nan")) == FA_ERR_INVALID_ARG
+    assert fwd(L, scale=float("inf")) == FA_ERR_INVALID_ARG
+    assert fwd(L, o=P) == FA_ERR_INVALID_ARG               # output aliases q
+    assert fwd(L, lse=P + 192 * MB + 64) == FA_ERR_INVALID_ARG   # lse inside o
+    assert fwd(L, B=65536, H=65536) == FA_ERR_INVALID_ARG  # row count beyond 32-bit
+    assert L.fa_fwd_ex(ctypes.c_void_p(P), ctypes.c_void_p(P + 64 * MB), ctypes.c_void_p(P + 128 * MB), 1, 1, 128,
+                       64, 0, ctypes.c_float(0.125), ctypes.c_void_p(P + 192 * MB), ctypes.c_void_p(P + 256 * MB),
+                       None, 99) == FA_ERR_UNSUPPORTED     # unknown tile configuration
+
+
+def bwd(L, variant=1, ws=P + 900 * MB, ws_bytes=1 << 20, dq=P + 600 * MB, d=64, N=128, scale=0.125):
+    args = [ctypes.c_void_p(P + i * 64 * MB) for i in range(6)]   # q k v o lse dout
+    return L.fa_bwd(*args, 1, 1, N, d, 0, scale, variant, ctypes.c_void_p(dq), ctypes.c_void_p(P + 700 * MB),
+                    ctypes.c_void_p(P + 800 * MB), ctypes.c_void_p(ws), ws_bytes, None)
+
+
+def test_bwd_rejects_bad_arguments(L):
+    from exact_attention_102_amd import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
+    assert L.fa_bwd_workspace_size(1, 1, 128, 64, 1) == 512
+    assert L.fa_bwd_workspace_size(2, 3, 1000, 128, 0) == 24064
+    assert L.fa_bwd_workspace_size(1, 1, 0, 64, 1) == 0
+    assert bwd(L, variant=7) == FA_ERR_UNSUPPORTED
+    assert bwd(L, ws=0) == FA_ERR_WORKSPACE
+    assert bwd(L, ws_bytes=100) == FA_ERR_WORKSPACE
+    assert bwd(L, dq=P) == FA_ERR_INVALID_ARG              # dq aliases q
+    assert bwd(L, dq=P + 700 * MB) == FA_ERR_INVALID_ARG   # dq aliases dk
+    assert bwd(L, ws=P + 800 * MB) == FA_ERR_INVALID_ARG   # workspace aliases dv
+    assert bwd(L, d=192) == FA_ERR_UNSUPPORTED
+    assert bwd(L, scale=float("nan")) == FA_ERR_INVALID_ARG
+    assert L.fa_bwd_preprocess(None, ctypes.c_void_p(P), 1, 1, 8, 64, ctypes.c_void_p(P + MB), None, 0,
+                               None) == FA_ERR_INVALID_ARG
+    assert L.fa_bwd_preprocess(ctypes.c_void_p(P), ctypes.c_void_p(P + MB), 1, 1, 8, 64, ctypes.c_void_p(P + 2 * MB),
+                               None, 1, None) == FA_ERR_INVALID_ARG   # zero_dq without dq
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from exact_attention_102_amd import binding
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
+
+
+# ----------------------------------------------------------------------------- host-side accounting
+def test_flop_accounting_matches_the_pages():
+    from exact_attention_102_amd.flops import attention_flops, mfa_op_counts, pairs
+    g = json.load(open(os.path.join(GOLDEN, "mfa_op_counts.json")))
+    for d in (64, 128, 256):
+        for N in (1, 128, 2048):
+            c = mfa_op_counts(N, d, dispatches=g["dispatches_per_trial"])
+            for k, (a, b) in g["per_pair"].items():
+                assert c[k] == (a * d + b) * N * N * g["dispatches_per_trial"]
+    r = json.load(open(os.path.join(GOLDEN, "gemm_ratio.json")))
+    f = attention_flops(4, 16, 2048, 128, False)
+    assert f["fwd"] == 2 * r["gemms"]["forward"] * 128 * f["pairs"]
+    assert f["bwd_effective"] == 2 * r["gemms"]["backward_5gemm"] * 128 * f["pairs"]
+    assert f["bwd_7gemm_issued"] == 2 * r["gemms"]["backward_7gemm"] * 128 * f["pairs"]
+    assert f["bwd_7gemm_issued"] / f["bwd_effective"] == pytest.approx(r["ratio_7_over_5"])
+    assert r["h100_5gemm_bwd_tflops"] * r["ratio_7_over_5"] == pytest.approx(r["h100_7gemm_breakeven_tflops"])
+    assert pairs(2048, False, 4, 16) == 4 * 16 * 2048 * 2048
+    assert pairs(5, True) == 15 and pairs(1, True) == 1
+    assert pairs(2048, True) == sum(i + 1 for i in range(2048))
+
+
+def test_block_size_rule_toy_example():
+    from exact_attention_102_amd.flops import block_size_rule
+    g = json.load(open(os.path.join(GOLDEN, "block_size_rule.json")))
+    assert block_size_rule(g["M"], g["d"]) == g["block"]
+    # 160 KiB of LDS in bf16 elements: 81920 -> d=64: 320, d=128: 160, d=256: 80
+    assert [block_size_rule(81920, d) for d in (64, 128, 256)] == [320, 160, 80]
+
+
+def test_d_spectrum_matches_the_page():
+    from exact_attention_102_amd.flops import d_spectrum
+    g = json.load(open(os.path.join(GOLDEN, "d_spectrum.json")))
+    assert d_spectrum() == g["values"]
+    assert len(g["values"]) == 42
