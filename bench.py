@@ -1,0 +1,253 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step runs the whole path over the workload's synthetic bf16 inputs (already
+resident in HBM): for the non-causal and the causal mask, the forward, the
+5-GEMM backward (preprocess with dq zeroing, dK/dV kernel with fp32-atomic dQ)
+and the 7-GEMM backward (preprocess, dK/dV kernel, dQ kernel).  Every kernel is
+bracketed by HIP events on the stream it runs on; W untimed steps are followed
+by exactly K timed steps between two device synchronisations.
+
+Work accounting (masked tiles are not credited; pairs = unmasked score
+elements): forward 4 d pairs, backward 10 d pairs for either design (the
+5-GEMM count, as the 5-vs-7 comparison in "Potential algorithmic improvements
+for backward pass" is made); the 7-GEMM design issues 14 d pairs.  `value` is
+the step's credited TFLOP/s; one JSON line is printed at the end.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd/bwd TFLOPS and % of bf16 MFMA peak, hdim 128 N=2k-8k"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+KERNEL_SOURCES = {"fwd": "fa_fwd.hip", "dkdv": "fa_bwd.hip", "dkdv_atomic": "fa_bwd.hip", "dq": "fa_bwd.hip",
+                  "preprocess": "fa_bwd.hip"}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in sorted({KERNEL_SOURCES[kernel], "fa_device.h"}):
+        with open(os.path.join(ROOT, "exact_attention_102_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_flops(kernel: str, d: int, pairs: int) -> int:
+    """Algorithmic MFMA flops of one launch: 2 d flops per pair per GEMM."""
+    gemms = {"fwd": 2, "dkdv": 4, "dkdv_atomic": 5, "dq": 3}[kernel]
+    return 2 * gemms * d * pairs
+
+
+def preprocess_bytes(rows: int, d: int, zero_dq: bool) -> int:
+    """Compulsory HBM bytes of the preprocess kernel: O fp32 + dO bf16 read, delta (+ dq zeros) written."""
+    return rows * (4 * d + 2 * d + 4 + (4 * d if zero_dq else 0))
+
+
+def stored_traffic(kernel: str, mask: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None when the
+    kernel's source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get("kernels", {}).get("%s_%s" % (kernel, mask))
+    if not ent or ent.get("source_hash") != source_hash(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, causal_modes, heads):
+    """The fp64 oracle as it stands, timed on this host's cores over `heads` heads of the workload."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads
+    from exact_attention_102_amd.flops import attention_flops
+
+    cores = oracle.usable_cores()
+    workers = max(1, min(cores, len(heads)))
+    blas = max(1, cores // workers)
+    q, k, v, do = (workloads.bf16_to_f64(workloads.to_bf16(x)) for x in workloads.draw_workload(w))
+    flops = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=blas, user_api="blas"):
+        for causal in causal_modes:
+            oracle.attention_forward_batched(q, k, v, w.scale, causal, workers=workers, heads=heads)
+            oracle.attention_backward_batched(q, k, v, do, w.scale, causal, workers=workers, heads=heads)
+            f = attention_flops(1, len(heads), w.N, w.d, causal)
+            flops += f["fwd"] + f["bwd_effective"]
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers * blas, "kind": "oracle",
+            "sample": "%d of %d heads of %s, masks %s, fwd+bwd in fp64 numpy, %.1f s wall" % (
+                len(heads), w.B * w.H, w.name, "+".join("causal" if c else "full" for c in causal_modes), dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b4_h16_n2048_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=-1, help="heads in the oracle sample (-1: all)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (heads shard with no "
+              "exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_config_name,
+                                         fa_default_config, fa_fwd, lib)
+    from exact_attention_102_amd.flops import attention_flops, mfa_op_counts
+
+    lib()  # fail loudly if libfa.so is missing
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = workloads.WORKLOADS[args.workload]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    masks = [False, True] if not w.causal else [True]
+    log("workload %s B=%d H=%d N=%d d=%d masks=%s" % (w.name, B, H, N, d, masks))
+
+    q, k, v, do = (workloads.to_bf16(x).cuda() for x in workloads.draw_workload(w))
+    dev = torch.device("cuda")
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = torch.empty((B, H, N, d), **f32)
+    lse = torch.empty((B, H, N), **f32)
+    delta = torch.empty((B, H, N), **f32)
+    dq5, dk5, dv5 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+    dq7, dk7, dv7 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+    stream = torch.cuda.current_stream()
+
+    # event plan per mask: fwd | pre5 | dkdv_atomic | pre7 | dkdv | dq
+    kernels = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]
+
+    def step(record):
+        for mi, causal in enumerate(masks):
+            ev = record[mi] if record is not None else None
+            if ev:
+                ev[0].record(stream)
+            fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream)
+            if ev:
+                ev[1].record(stream)
+            fa_bwd_preprocess(o, do, delta=delta, dq=dq5, stream=stream)
+            if ev:
+                ev[2].record(stream)
+            fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, True, dk5, dv5, dq=dq5, stream=stream)
+            if ev:
+                ev[3].record(stream)
+            fa_bwd_preprocess(o, do, delta=delta, stream=stream)
+            if ev:
+                ev[4].record(stream)
+            fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, False, dk7, dv7, stream=stream)
+            if ev:
+                ev[5].record(stream)
+            fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq7, stream=stream)
+            if ev:
+                ev[6].record(stream)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in masks] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per (mask, kernel) mean duration in ms
+    dur = {}
+    for mi, causal in enumerate(masks):
+        mname = "causal" if causal else "full"
+        for ki, kn in enumerate(kernels):
+            ts = [events[s][mi][ki].elapsed_time(events[s][mi][ki + 1]) for s in range(args.steps)]
+            dur[(mname, kn)] = (sum(ts) / len(ts), min(ts))
+
+    total_flops = 0
+    passes = {}
+    best = None
+    for causal in masks:
+        mname = "causal" if causal else "full"
+        fl = attention_flops(B, H, N, d, causal)
+        p = fl["pairs"]
+        t_fwd = dur[(mname, "fwd")][0]
+        t_b5 = dur[(mname, "preprocess5")][0] + dur[(mname, "dkdv_atomic")][0]
+        t_b7 = dur[(mname, "preprocess7")][0] + dur[(mname, "dkdv")][0] + dur[(mname, "dq")][0]
+        total_flops += fl["fwd"] + 2 * fl["bwd_effective"]
+        passes[mname] = {
+            "fwd_tflops": fl["fwd"] / t_fwd / 1e9, "fwd_ms": t_fwd,
+            "bwd_5gemm_tflops": fl["bwd_effective"] / t_b5 / 1e9, "bwd_5gemm_ms": t_b5,
+            "bwd_7gemm_tflops": fl["bwd_effective"] / t_b7 / 1e9, "bwd_7gemm_ms": t_b7,
+            "bwd_7gemm_issued_tflops": fl["bwd_7gemm_issued"] / t_b7 / 1e9,
+            "kernel_ms": {kn: round(dur[(mname, kn)][0], 4) for kn in kernels},
+            "pairs": p,
+        }
+        for key in ("fwd", "bwd_5gemm", "bwd_7gemm"):
+            passes[mname][key + "_pct_peak"] = 100.0 * passes[mname][key + "_tflops"] / PEAK_BF16_TFLOPS
+        passes[mname]["faster_bwd"] = "5gemm" if t_b5 <= t_b7 else "7gemm"
+        passes[mname]["t7_over_t5"] = t_b7 / t_b5
+        for kn in ("fwd", "dkdv_atomic", "dkdv", "dq"):
+            t = dur[(mname, kn)][0]
+            if best is None or t > best[2]:
+                best = (kn, mname, t, kernel_flops(kn, d, p))
+    op_counts = mfa_op_counts(N, d)
+
+    kn, mname, t_ms, kflops = best
+    achieved = kflops / (t_ms * 1e-3) / 1e12
+    traffic = stored_traffic(kn, mname, w.name)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "%s (%s mask)" % (kn, mname), "launch_ms": round(t_ms, 4),
+                "flops_per_launch": kflops}
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        heads = list(range(B * H)) if args.cpu_heads < 0 else list(range(min(args.cpu_heads, B * H)))
+        log("timing the fp64 oracle on %d heads" % len(heads))
+        cpu = cpu_baseline(w, masks, heads)
+
+    cfgs = {"fwd": fa_config_name(0, d, False, fa_default_config(0, d)),
+            "dkdv": fa_config_name(1, d, False, fa_default_config(1, d)),
+            "dkdv_atomic": fa_config_name(2, d, False, fa_default_config(2, d)),
+            "dq": fa_config_name(3, d, False, fa_default_config(3, d))}
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name + (" (non-causal + causal)" if len(masks) == 2 else ""), "B": B, "H": H,
+                   "N": N, "d": d, "scale": w.scale, "step": "per mask: fwd + 5-GEMM bwd + 7-GEMM bwd",
+                   "tiles": cfgs},
+        "passes": {m: {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in p.items()}
+                   for m, p in passes.items()},
+        "mfa_op_counts_per_dispatch": op_counts,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_ex.restype = i
     L.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, vp, i, vp]
     L.fa_bwd_preprocess.restype = i
+    L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, i]
+    L.fa_bwd_dkdv.restype = i
+    L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, i]
+    L.fa_bwd_dq.restype = i
     L.fa_num_configs.argtypes = [i, i, i]
     L.fa_num_configs.restype = i
     L.fa_config_name.argtypes = [i, i, i, i, cp, sz]
@@ -185,3 +189,34 @@ def fa_bwd_preprocess(o, dout, delta=None, dq=None, stream=None):
     if st != FA_OK:
         raise FAError(st, "fa_bwd_preprocess")
     return delta
+
+
+def fa_bwd_dkdv(q, k, v, dout, lse, delta, causal: bool, scale: float, atomic_dq: bool, dk, dv, dq=None,
+                stream=None, cfg: int = -1):
+    """dK/dV kernel stage (plus fp32-atomic dQ when atomic_dq); outputs must be allocated by the caller."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    ptr = [_check(q, "q", torch.bfloat16), _check(k, "k", torch.bfloat16, q.shape),
+           _check(v, "v", torch.bfloat16, q.shape), _check(dout, "dout", torch.bfloat16, q.shape),
+           _check(lse, "lse", torch.float32, (B, H, N)), _check(delta, "delta", torch.float32, (B, H, N))]
+    pq = _check(dq, "dq", torch.float32, q.shape) if atomic_dq else ctypes.c_void_p(0)
+    st = lib().fa_bwd_dkdv(*ptr, B, H, N, d, int(bool(causal)), float(scale), int(bool(atomic_dq)), pq,
+                           _check(dk, "dk", torch.float32, q.shape), _check(dv, "dv", torch.float32, q.shape),
+                           _stream_ptr(stream), int(cfg))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dkdv")
+    return dk, dv
+
+
+def fa_bwd_dq(q, k, v, dout, lse, delta, causal: bool, scale: float, dq, stream=None, cfg: int = -1):
+    """dQ kernel stage of the 7-GEMM design; dq must be allocated by the caller."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    ptr = [_check(q, "q", torch.bfloat16), _check(k, "k", torch.bfloat16, q.shape),
+           _check(v, "v", torch.bfloat16, q.shape), _check(dout, "dout", torch.bfloat16, q.shape),
+           _check(lse, "lse", torch.float32, (B, H, N)), _check(delta, "delta", torch.float32, (B, H, N))]
+    st = lib().fa_bwd_dq(*ptr, B, H, N, d, int(bool(causal)), float(scale), _check(dq, "dq", torch.float32, q.shape),
+                         _stream_ptr(stream), int(cfg))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dq")
+    return dq

@@ -214,6 +214,87 @@ fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int 
   return launched();
 }
 
+namespace {
+
+fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                     const float* delta, int B, int H, int N, float scale, float* dq, float* dk, float* dv) {
+  fa::BwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.dout = static_cast<const __bf16*>(dout);
+  a.lse = lse;
+  a.delta = delta;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  return a;
+}
+
+// Validation shared by the backward stages: read-only inputs q k v dout (bf16), lse and delta
+// (fp32 rows); outputs must be 16-B aligned and overlap neither the inputs nor each other.
+fa_status check_bwd_stage(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                          const float* delta, int B, int H, int N, int d, float scale, float* const* outs,
+                          int n_outs) {
+  if (!q || !k || !v || !dout || !lse || !delta) return FA_ERR_INVALID_ARG;
+  const void* in_ptrs[] = {q, k, v, dout, lse, delta};
+  for (const void* p : in_ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  for (int i = 0; i < n_outs; ++i)
+    if (!outs[i] || !aligned16(outs[i])) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_sizes(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  const size_t elems = (size_t)B * H * N * d;
+  const size_t rows = (size_t)B * H * N;
+  const Range ins[] = {rng(q, elems * 2), rng(k, elems * 2), rng(v, elems * 2),
+                       rng(dout, elems * 2), rng(lse, rows * 4), rng(delta, rows * 4)};
+  for (int i = 0; i < n_outs; ++i) {
+    const Range ro = rng(outs[i], elems * 4);
+    for (const Range& r : ins)
+      if (overlaps(ro, r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < n_outs; ++j)
+      if (overlaps(ro, rng(outs[j], elems * 4))) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, int B, int H, int N, int d, int causal, float scale, int atomic_dq,
+                      float* dq, float* dk, float* dv, void* stream, int cfg) {
+  float* outs[3] = {dk, dv, dq};
+  const fa_status st = check_bwd_stage(q, k, v, dout, lse, delta, B, H, N, d, scale, outs, atomic_dq ? 3 : 2);
+  if (st != FA_OK) return st;
+  const int pass = atomic_dq ? 2 : 1;
+  int n = 0;
+  const BwdConfig* t = bwd_table(pass, &n);
+  const int j = nth_for_d(t, n, d, cfg < 0 ? default_index(pass, d, causal) : cfg);
+  if (j < 0) return FA_ERR_UNSUPPORTED;
+  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, atomic_dq ? dq : nullptr, dk, dv);
+  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                    const float* delta, int B, int H, int N, int d, int causal, float scale, float* dq,
+                    void* stream, int cfg) {
+  float* outs[1] = {dq};
+  const fa_status st = check_bwd_stage(q, k, v, dout, lse, delta, B, H, N, d, scale, outs, 1);
+  if (st != FA_OK) return st;
+  int n = 0;
+  const BwdConfig* t = bwd_table(3, &n);
+  const int j = nth_for_d(t, n, d, cfg < 0 ? default_index(3, d, causal) : cfg);
+  if (j < 0) return FA_ERR_UNSUPPORTED;
+  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, nullptr, nullptr);
+  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
 fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                     int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
                     float* dv, void* workspace, size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq) {
@@ -264,20 +345,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
   fa_status st = launched();
   if (st != FA_OK) return st;
 
-  fa::BwdArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
-  a.dout = static_cast<const __bf16*>(dout);
-  a.lse = lse;
-  a.delta = delta;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.scale = scale;
+  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv);
   if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   st = launched();
   if (st != FA_OK || atomic) return st;

@@ -99,6 +99,21 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
 fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int N, int d, float* delta,
                             float* dq, int zero_dq, void* stream);
 
+/* The backward's two kernel stages on their own (fa_bwd runs preprocess, then
+ * these).  delta must hold the preprocess result for the same o/dout.
+ * fa_bwd_dkdv: dk, dv (fp32 [B,H,N,d], written).  With atomic_dq != 0 it also adds
+ *   scale * dS K into dq with fp32 atomics (the 5-GEMM design; dq must already be
+ *   zero or hold a partial sum); with atomic_dq == 0, dq is ignored (may be NULL).
+ * fa_bwd_dq: the 7-GEMM design's dQ kernel; dq (fp32 [B,H,N,d]) is written once per
+ *   element, no atomics.
+ * cfg: tile configuration index (-1 = default) of pass 1/2 (dkdv) or 3 (dq). */
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                      const float* delta, int B, int H, int N, int d, int causal, float scale, int atomic_dq,
+                      float* dq, float* dk, float* dv, void* stream, int cfg);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                    const float* delta, int B, int H, int N, int d, int causal, float scale, float* dq,
+                    void* stream, int cfg);
+
 /* Tile configurations, for the block-shape sweep ("Potential algorithmic
  * improvements for backward pass": search over block dimensions under register
  * pressure; non-square blocks such as 32-64 x 160-320).
