@@ -51,20 +51,26 @@ __device__ __forceinline__ int pi_row(int R) {
 
 // ---------------------------------------------------------------------------
 // Swizzled LDS tile of bf16, W elements per row (row pitch 2W bytes, no padding).
-// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r).  The XOR
-// pattern keeps both access shapes free of bank conflicts on a 64-bank LDS:
-//  * row fragments: 16 lanes read the same chunk of 16 distinct rows;
-//  * transposed reads: 32 lanes read 4 consecutive rows x 64 contiguous bytes;
-//  * staging writes: 16 lanes write 256 contiguous bytes.
+// The 16-byte chunk c of row r is stored at chunk position c ^ swz(r).  Two read
+// shapes must both avoid LDS bank conflicts (64 banks of 4 bytes):
+//  * row fragments (ds_read_b128): each group of 8 lanes reads the same chunk of
+//    8 distinct rows {R..R+3, R+8..R+11};
+//  * transposed reads (ds_read_b64_tr_b16): 16 lanes read 4 consecutive rows x 32
+//    contiguous bytes, a half-wave 4 rows x 64 bytes.  Measured on gfx950, these
+//    slow down when the XOR flips the lowest chunk bit (it reorders the two 16-byte
+//    halves of a 32-byte row segment), so the swizzle only touches bits 1..3.
+// swz = 4 (r % 4) ^ 2 ((r / 8) % 2) puts the 4 consecutive rows of a transposed
+// read in 4 different 64-byte quarters and the 8 rows of a row-fragment group on 8
+// different 16-byte bank groups.  (W = 64 packs two rows per 256-byte bank line
+// and uses the analogous bits; W = 32 is only read transposed.)
 template <int W>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (W == 32) {
-    return (row >> 2) & 3;
+    return ((row >> 2) & 1) << 1;
   } else if constexpr (W == 64) {
-    const int x = (row >> 1) & 7;
-    return ((x & 1) << 2) | (x >> 1);
+    return (((row >> 1) & 1) << 2) ^ (((row >> 3) & 1) << 1);
   } else {
-    return ((row & 3) << 2) | ((row >> 2) & 3);
+    return ((row & 3) << 2) ^ (((row >> 3) & 1) << 1);
   }
 }
 
@@ -126,6 +132,36 @@ struct TileStager {
   }
 };
 
+// Direct-to-LDS copy of a ROWS x W bf16 tile (global_load_lds_dwordx4): each wave
+// instruction moves 64 x 16 bytes straight into 1 KB of contiguous LDS (lane l
+// lands at base + 16 l), bypassing registers.  Lane l therefore fetches the global
+// chunk that belongs at its LDS position under the swizzle.  Rows at or beyond
+// valid_rows are clamped to the last valid row: the kernels mask such keys (-inf
+// scores) and give such queries P = 0, so the duplicated data never contributes.
+// The copy is asynchronous: wait_tile() (vmcnt) plus a barrier must precede reads.
+template <int ROWS, int W, int NW>
+struct TileDMA {
+  static constexpr int kPieces = ROWS * W * 2 / 1024;
+  static constexpr int kPerWave = kPieces / NW;
+  static_assert(kPieces % NW == 0, "tile must split into whole 1 KB pieces per wave");
+  __device__ __forceinline__ static void issue(const __bf16* g, int row0, int valid_rows, LDS char* tile, int wave,
+                                               int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int piece = i * NW + wave;
+      const int byte = piece * 1024 + lane * 16;
+      const int row = byte / (2 * W);
+      const int p = (byte % (2 * W)) >> 4;
+      const int c = p ^ swz<W>(row);
+      const int grow = min(row0 + row, valid_rows - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + (size_t)grow * W + c * 8),
+                                       (LDS void*)(tile + piece * 1024), 16, 0, 0);
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_tile() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------------------
 // Reductions across the two 32-lane halves (lane l and lane l ^ 32), which hold
 // the two halves of a 32-key (or 32-query) block in the C layout.
@@ -141,6 +177,19 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 }
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + sum of the 8 bf16 values, accumulated in fp32 (v_dot2c_f32_bf16 against 1.0).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, acc, false);
+  }
+  return acc;
+}
 
 __device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
   bf16x8 r;

@@ -1,34 +1,127 @@
 // fa_fwd.hip -- fused attention forward for gfx950.
 //
-// One workgroup owns BR = 32 * QB * NW query rows of one (batch, head); each of
-// its NW waves owns 32 * QB of them.  The workgroup walks the key/value tiles
-// (BC keys each) through double-buffered LDS ("ELI5: FlashAttention": tiling and
-// kernel fusion -- S and P live only in registers), and keeps, per query row,
-// the running maximum m and running exp-sum l of the online softmax (same page,
-// the m(x)/l(x) statistics).  Per tile:
+// One workgroup owns BR = 32 * NW query rows of one (batch, head); each of its NW
+// waves owns 32 of them, one per MFMA lane column.  The workgroup walks the
+// key/value tiles (BC keys each) through double-buffered LDS ("ELI5:
+// FlashAttention": tiling and kernel fusion -- S and P live only in registers), and
+// keeps, per query row, the running maximum m and running exp-sum l of the online
+// softmax (same page, the m(x)/l(x) statistics).  Per tile:
 //   S^T = K Q^T          MFMA, A = K row fragments from LDS, B = Q^T in registers
 //   mask, row max        in-lane over 16 keys per 32-key block + one half swap
 //   P^T = exp2(S^T * c - m)   c = scale * log2(e) folded into one FMA
 //   O^T += V^T P^T       MFMA, A = V^T via transposed LDS reads, B = P^T from
 //                        the S^T accumulators (bf16, round-to-nearest-even)
-// The transposed orientation (keys down the MFMA rows, one query per lane
-// column) keeps every row statistic in-lane.  The epilogue writes O = O^T / l in
-// fp32 and lse = ln(2) * (m + log2 l).
+// The transposed orientation (keys down the MFMA rows, one query per lane column)
+// keeps every row statistic in-lane.  K/V tiles move HBM -> LDS by direct-to-LDS
+// loads issued one tile ahead, so no registers stage them.
+//
+// Rescaling is lazy: m only moves (and O, l are rescaled by exp2(m_old - m_new))
+// when some row's tile maximum exceeds its running m by more than kRescaleSlack
+// (in log2 units).  Otherwise P is computed against the stale m, so P <= 2^slack;
+// the result is unchanged in exact arithmetic because O and l carry the same
+// factor and the final O / l cancels it, and lse uses the m actually applied.
+// Two row sums are kept: l of the fp32 P (for lse) and l~ of the bf16-rounded P
+// that the PV product actually consumes (one v_dot2c_f32_bf16 per pair).  O is
+// divided by l~, so a row whose softmax is one-hot returns exactly that V row
+// even when its dominant P is not a power of two; lse = ln(2) * (m + log2 l).
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 
-template <int D, int BC, int NW, int QB, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
-  constexpr int BR = 32 * QB * NW;
-  constexpr int NT = NW * 64;
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D, int BC, bool CAUSAL>
+struct FwdTileMath {
+  static constexpr int KB = BC / 32;  // 32-key blocks per tile
+  static constexpr int DB = D / 32;   // 32-wide blocks of the head dim
+  static constexpr int KK = D / 16;   // k-steps of Q K^T
+
+  // One K/V tile for one wave: 32 queries (one per lane column) x BC keys.
+  __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
+                                              f32x16 (&o)[DB], float& m_run, float& l_run, float& lb_run, int k0,
+                                              int q_w, int qi, int N, float c, int krow, int g, int lane) {
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(row_frag<D>(kt, kb * 32 + krow, kk * 16 + g * 8), qf[kk], s[kb]);
+    }
+    // keys past the end, and (causal) keys after the query, score -inf
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (key >= N || (CAUSAL && key > qi)) s[kb][r] = -INFINITY;
+        }
+      }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    }
+    mx = half_swap_max(mx) * c;
+    // Tile 0 holds key 0 <= every query, so m_run is finite after the first tile.
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = exp2_hw(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      lb_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+    }
+    const float nm = -m_run;
+    bf16x8 pb[2 * KB];
+    float rs = 0.f, rb = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(fmaf(s[kb][r], c, nm));
+        s[kb][r] = p;
+        rs += p;
+      }
+      pb[2 * kb] = pack8(s[kb], 0);
+      pb[2 * kb + 1] = pack8(s[kb], 8);
+      rb = sum_bf16x8(pb[2 * kb], rb);
+      rb = sum_bf16x8(pb[2 * kb + 1], rb);
+    }
+    l_run += rs;
+    lb_run += rb;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(col_frag<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
+    }
+  }
+};
+
+// OCC: waves per SIMD the register allocation must allow (2 lets a second wave's
+// MFMAs overlap this wave's softmax; d = 256 needs the whole register file).
+template <int D, int BC, int NW, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
+  using M = FwdTileMath<D, BC, CAUSAL>;
+  constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;  // bytes of one K or V tile
-  constexpr int KB = BC / 32;       // 32-key blocks per tile
-  constexpr int DB = D / 32;        // 32-wide blocks of the head dim
-  constexpr int KK = D / 16;        // k-steps of Q K^T
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE];
-  LDS char* smem = (LDS char*)smem_raw;
+  constexpr int DB = M::DB, KK = M::KK;
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+  LDS char* kbuf0 = (LDS char*)k0s;
+  LDS char* vbuf0 = (LDS char*)v0s;
+  LDS char* kbuf1 = (LDS char*)k1s;
+  LDS char* vbuf1 = (LDS char*)v1s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -44,180 +137,89 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;
 
   const int q_wg = qt * BR;
-  const int q_w = q_wg + wave * 32 * QB;
-
-  bf16x8 qf[QB][KK];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qi = q_w + qb * 32 + l32;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (qi < N) {
-        qf[qb][kk] = *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + g * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[qb][kk][e] = (__bf16)0.f;
-      }
-    }
-  }
-
-  float m_run[QB], l_run[QB];
-  f32x16 o[QB][DB];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = zero16();
-  }
-
+  const int q_w = q_wg + wave * 32;
+  const int qi = q_w + l32;
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
+  using DMA = TileDMA<BC, D, NW>;
+
+  DMA::issue(Kh, 0, N, kbuf0, wave, lane);
+  DMA::issue(Vh, 0, N, vbuf0, wave, lane);
+
+  bf16x8 qf[KK];
+  const int qrow = min(qi, N - 1);  // rows past the end duplicate the last row; never stored
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(Qh + (size_t)qrow * D + kk * 16 + g * 8);
+
+  float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = zero16();
   const int krow = pi_row(l32);
 
-  TileStager<BC, D, NT> sk, sv;
-  sk.load(Kh, 0, N, tid);
-  sv.load(Vh, 0, N, tid);
-  sk.store(smem, tid);
-  sv.store(smem + TILE, tid);
+  wait_tile();
   __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const LDS char* kt = smem + (j & 1) * 2 * TILE;
-    const LDS char* vt = kt + TILE;
-    const bool more = j + 1 < nkt;
-    if (more) {
-      sk.load(Kh, (j + 1) * BC, N, tid);
-      sv.load(Vh, (j + 1) * BC, N, tid);
+  for (int j = 0; j < nkt; j += 2) {
+    if (j + 1 < nkt) {
+      DMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      DMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
-    const int k0 = j * BC;
-    const bool active = !CAUSAL || k0 <= q_w + 32 * QB - 1;
-    if (active) {
-      f32x16 s[QB][KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 ka = row_frag<D>(kt, kb * 32 + krow, kk * 16 + g * 8);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma32(ka, qf[qb][kk], s[qb][kb]);
-        }
-      }
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qi = q_w + qb * 32 + l32;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-              if (key >= N || (CAUSAL && key > qi)) s[qb][kb][r] = -INFINITY;
-            }
-          }
-        }
-      }
-      bf16x8 pb[QB][2 * KB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-        }
-        mx = half_swap_max(mx);
-        const float m_new = fmaxf(m_run[qb], mx * c);
-        const float alpha = exp2_hw(m_run[qb] - m_new);
-        m_run[qb] = m_new;
-        const float nm = -m_new;
-        float rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = exp2_hw(fmaf(s[qb][kb][r], c, nm));
-            s[qb][kb][r] = p;
-            rs += p;
-          }
-          pb[qb][2 * kb] = pack8(s[qb][kb], 0);
-          pb[qb][2 * kb + 1] = pack8(s[qb][kb], 8);
-        }
-        l_run[qb] = l_run[qb] * alpha + rs;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[qb][db][r] *= alpha;
-        }
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 2 * KB; ++ks) {
-          const bf16x8 va = col_frag<D>(vt, ks * 16, db * 32, lane);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma32(va, pb[qb][ks], o[qb][db]);
-        }
-      }
+    if (!CAUSAL || j * BC <= q_w + 31)
+      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, krow, g, lane);
+    wait_tile();
+    __syncthreads();
+    if (j + 1 >= nkt) break;
+    if (j + 2 < nkt) {
+      DMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      DMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
-    if (more) {
-      LDS char* nt = smem + ((j + 1) & 1) * 2 * TILE;
-      sk.store(nt, tid);
-      sv.store(nt + TILE, tid);
-    }
+    if (!CAUSAL || (j + 1) * BC <= q_w + 31)
+      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, krow, g, lane);
+    wait_tile();
     __syncthreads();
   }
 
-  float* Oh = a.o + head;
-  float* Lh = a.lse + (size_t)bh * N;
+  const float lt = half_swap_sum(l_run);
+  const float inv = 1.f / half_swap_sum(lb_run);
+  if (qi < N) {
+    float* orow = a.o + head + (size_t)qi * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = half_swap_sum(l_run[qb]);
-    const float inv = 1.f / lt;
-    const int qi = q_w + qb * 32 + l32;
-    if (qi < N) {
-      float* orow = Oh + (size_t)qi * D;
+    for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 val = {o[qb][db][4 * a4] * inv, o[qb][db][4 * a4 + 1] * inv, o[qb][db][4 * a4 + 2] * inv,
-                             o[qb][db][4 * a4 + 3] * inv};
-          *(f32x4*)(orow + db * 32 + 8 * a4 + 4 * g) = val;
-        }
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 val = {o[db][4 * a4] * inv, o[db][4 * a4 + 1] * inv, o[db][4 * a4 + 2] * inv,
+                           o[db][4 * a4 + 3] * inv};
+        *(f32x4*)(orow + db * 32 + 8 * a4 + 4 * g) = val;
       }
-      if (g == 0) Lh[qi] = (m_run[qb] + log2f(lt)) * kLn2;
     }
+    if (g == 0) a.lse[(size_t)bh * N + qi] = (m_run + log2f(lt)) * kLn2;
   }
 }
 
-template <int D, int BC, int NW, int QB>
+template <int D, int BC, int NW, int OCC>
 static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
-  constexpr int BR = 32 * QB * NW;
+  constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.H * nqt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if (causal) {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, QB, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, QB, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   }
   return 0;
 }
 
-#define FWD_CFG(D, BC, NW, QB) \
-  { D, 32 * (QB) * (NW), BC, NW, "fwd d" #D " Br" #QB "x32x" #NW " Bc" #BC, &launch_fwd<D, BC, NW, QB> }
+#define FWD_CFG(D, BC, NW, OCC) \
+  { D, 32 * (NW), BC, NW, "fwd d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, BC, NW, OCC> }
 
 // Host-side table (function-local so that only the host pass materialises it).
 const FwdConfig* fwd_configs(int* count) {
   static const FwdConfig table[] = {
-      FWD_CFG(64, 64, 4, 1),  FWD_CFG(64, 128, 4, 1), FWD_CFG(64, 64, 4, 2),
-      FWD_CFG(128, 64, 4, 1), FWD_CFG(128, 32, 4, 2), FWD_CFG(128, 128, 4, 1),
-      FWD_CFG(256, 32, 4, 1),
+      FWD_CFG(64, 64, 4, 2),   FWD_CFG(64, 128, 4, 2),  FWD_CFG(64, 64, 8, 2),  FWD_CFG(64, 128, 8, 2),
+      FWD_CFG(128, 64, 4, 2),  FWD_CFG(128, 32, 4, 2),  FWD_CFG(128, 64, 8, 2), FWD_CFG(128, 128, 4, 1),
+      FWD_CFG(256, 32, 4, 1),  FWD_CFG(256, 64, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
