@@ -92,9 +92,10 @@ struct RowStager {
 // dK/dV kernel.  One workgroup owns BK = 32 * NW keys of one (batch, head), each
 // wave 32 of them (one key per lane column of the MFMA C layout).  It walks the
 // query tiles (BQ rows of Q and dO, plus their lse and delta) through
-// double-buffered LDS.  Per 32-query block:
+// double-buffered LDS, the Q/dO rows arriving by direct-to-LDS loads one tile
+// ahead.  Per 32-query block:
 //   S  = Q K^T,  dP = dO V^T          A = Q / dO row fragments (LDS),
-//                                      B = K^T / V^T (registers or LDS)
+//                                      B = K^T / V^T (registers, or LDS if KV_LDS)
 //   P, dS                              elementwise, in registers
 //   dV^T += dO^T P,  dK^T += Q^T dS    A = transposed LDS reads, B = P / dS
 // ATOMIC (the 5-GEMM design): each wave also writes its dS^T block to LDS; after a
@@ -103,162 +104,96 @@ struct RowStager {
 // per dq element per workgroup and query tile.
 // KV_LDS keeps the workgroup's K and V in LDS instead of registers (large d).
 template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS>
-__global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
-  constexpr int BK = 32 * NW;
-  constexpr int NT = NW * 64;
-  constexpr int QTILE = BQ * D * 2;
-  constexpr int STAGE = 2 * QTILE + 2 * BQ * 4;
-  constexpr int QBN = BQ / 32;
-  constexpr int DB = D / 32;
-  constexpr int KK = D / 16;
-  constexpr int KT_BYTES = (ATOMIC || KV_LDS) ? BK * D * 2 : 0;
-  constexpr int VT_BYTES = KV_LDS ? BK * D * 2 : 0;
-  constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 0;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[2 * STAGE + KT_BYTES + VT_BYTES + DST_BYTES];
-  LDS char* smem = (LDS char*)smem_raw;
-  LDS char* ktile = smem + 2 * STAGE;
-  LDS char* vtile = ktile + KT_BYTES;
-  LDS char* dst = vtile + VT_BYTES;
+struct DkdvMath {
+  static constexpr int BK = 32 * NW;
+  static constexpr int QBN = BQ / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int KK = D / 16;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int N = a.N;
-  const int nkt = (N + BK - 1) / BK;
-  const int item = xcd_remap(blockIdx.x, a.B * a.H * nkt);
-  const int bh = item / nkt;
-  const int kt = item % nkt;  // causal: low key tiles see the most queries and come first
-  const size_t head = (size_t)bh * N * D;
-  const __bf16* Qh = a.q + head;
-  const __bf16* Kh = a.k + head;
-  const __bf16* Vh = a.v + head;
-  const __bf16* dOh = a.dout + head;
-  const float* lseh = a.lse + (size_t)bh * N;
-  const float* delh = a.delta + (size_t)bh * N;
-  const float c = a.scale * kLog2e;
-
-  const int k0 = kt * BK;
-  const int kw = k0 + wave * 32;
-  const int key = kw + l32;
-
-  if constexpr (ATOMIC || KV_LDS) {
-    TileStager<BK, D, NT> st;
-    st.load(Kh, k0, N, tid);
-    st.store(ktile, tid);
-    if constexpr (KV_LDS) {
-      st.load(Vh, k0, N, tid);
-      st.store(vtile, tid);
-    }
-  }
-  bf16x8 kf[KV_LDS ? 1 : KK], vf[KV_LDS ? 1 : KK];
-  if constexpr (!KV_LDS) {
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      if (key < N) {
-        kf[kk] = *(const bf16x8*)(Kh + (size_t)key * D + kk * 16 + g * 8);
-        vf[kk] = *(const bf16x8*)(Vh + (size_t)key * D + kk * 16 + g * 8);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          kf[kk][e] = (__bf16)0.f;
-          vf[kk][e] = (__bf16)0.f;
-        }
-      }
-    }
-  }
-
-  f32x16 dk[DB], dv[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dk[db] = zero16();
-    dv[db] = zero16();
-  }
-
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? k0 / BQ : 0;
-  const int qrow = pi_row(l32);
-
-  TileStager<BQ, D, NT> sq, sdo;
-  RowStager<BQ, NT> srow;
-  sq.load(Qh, qt0 * BQ, N, tid);
-  sdo.load(dOh, qt0 * BQ, N, tid);
-  srow.load(lseh, delh, qt0 * BQ, N, tid);
-  sq.store(smem, tid);
-  sdo.store(smem + QTILE, tid);
-  srow.store((LDS float*)(smem + 2 * QTILE), tid);
-  __syncthreads();
-
-  for (int it = qt0; it < nqt; ++it) {
-    const int buf = (it - qt0) & 1;
-    const LDS char* qtl = smem + buf * STAGE;
-    const LDS char* dotl = qtl + QTILE;
-    const LDS float* l2t = (const LDS float*)(qtl + 2 * QTILE);
-    const LDS float* dlt = l2t + BQ;
-    const bool more = it + 1 < nqt;
-    if (more) {
-      sq.load(Qh, (it + 1) * BQ, N, tid);
-      sdo.load(dOh, (it + 1) * BQ, N, tid);
-      srow.load(lseh, delh, (it + 1) * BQ, N, tid);
-    }
-    const int q0 = it * BQ;
+  __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
+                                              const LDS char* ktile, const LDS char* vtile, LDS char* dst,
+                                              const bf16x8* kf, const bf16x8* vf, f32x16 (&dk)[DB],
+                                              f32x16 (&dv)[DB], float* dqh, int q0, int k0, int kw, int key, int N,
+                                              float c, float scale, const FragOffsets<D>& fo,
+                                              const PlainRowOffsets<D>& po, int wave, int g, int l32, int lane) {
+    const LDS float* l2t = stats;
+    const LDS float* dlt = stats + BQ;
 #pragma unroll
     for (int qb = 0; qb < QBN; ++qb) {
       const int qbase = q0 + qb * 32;
-      const bool active = !CAUSAL || qbase + 31 >= kw;
-      if (active) {
+      // Scheduling fences between the phases keep the live register set to one
+      // phase's operands (otherwise every LDS read of the tile is hoisted up front).
+      __builtin_amdgcn_sched_barrier(0);
+      // Blocks wholly past the end (padding rows, P = 0), or wholly above the causal
+      // diagonal for this wave's keys, contribute nothing.
+      if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 qa = row_frag<D>(qtl, qb * 32 + qrow, kk * 16 + g * 8);
-          const bf16x8 da = row_frag<D>(dotl, qb * 32 + qrow, kk * 16 + g * 8);
           bf16x8 kb, vb;
           if constexpr (KV_LDS) {
-            kb = row_frag<D>(ktile, wave * 32 + l32, kk * 16 + g * 8);
-            vb = row_frag<D>(vtile, wave * 32 + l32, kk * 16 + g * 8);
+            kb = po.row(ktile, wave * 32, kk);
+            vb = po.row(vtile, wave * 32, kk);
           } else {
             kb = kf[kk];
             vb = vf[kk];
           }
-          s = mfma32(qa, kb, s);
-          dp = mfma32(da, vb, dp);
+          s = mfma32(fo.row(qtl, qb * 32, kk), kb, s);
+          dp = mfma32(fo.row(dotl, qb * 32, kk), vb, dp);
+          fence_every<4>(kk);
         }
+        __builtin_amdgcn_sched_barrier(0);
         // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
         float l2[16], dl[16];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int r = qb * 32 + 16 * h + 8 * g + 4 * half;
+          for (int hf = 0; hf < 2; ++hf) {
+            const int r = qb * 32 + 16 * h + 8 * g + 4 * hf;
             const f32x4 lv = *(const LDS f32x4*)(l2t + r);
             const f32x4 dd = *(const LDS f32x4*)(dlt + r);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              l2[8 * h + 4 * half + e] = lv[e];
-              dl[8 * h + 4 * half + e] = dd[e];
+              l2[8 * h + 4 * hf + e] = lv[e];
+              dl[8 * h + 4 * hf + e] = dd[e];
             }
           }
         }
-        const bool need_mask = (k0 + BK > N) || (CAUSAL && qbase < kw + 31);
+        // Queries past the end have lse2 = +inf, hence P = 0.  Keys past the end only
+        // feed their own dK/dV columns, which are never stored -- except through dS in
+        // the atomic dQ product, where their dS^T rows are written as zeros below.
+        // Under the causal mask, key > query covers them as well.
+        const bool need_mask = CAUSAL && qbase < kw + 31;
         f32x16 p, ds;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = exp2_hw(fmaf(s[r], c, -l2[r]));
           if (need_mask) {
             const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
-            if (key >= N || (CAUSAL && key > q)) pv = 0.f;
+            if (key > q) pv = 0.f;
           }
           p[r] = pv;
           ds[r] = pv * (dp[r] - dl[r]);
         }
         const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-        const bf16x8 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
+        bf16x8 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(col_frag<D>(dotl, qb * 32, db * 32, lane), pb0, dv[db]);
-          dv[db] = mfma32(col_frag<D>(dotl, qb * 32 + 16, db * 32, lane), pb1, dv[db]);
-          dk[db] = mfma32(col_frag<D>(qtl, qb * 32, db * 32, lane), sb0, dk[db]);
-          dk[db] = mfma32(col_frag<D>(qtl, qb * 32 + 16, db * 32, lane), sb1, dk[db]);
+          dv[db] = mfma32(fo.col(dotl, qb * 32, db), pb0, dv[db]);
+          dv[db] = mfma32(fo.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+          dk[db] = mfma32(fo.col(qtl, qb * 32, db), sb0, dk[db]);
+          dk[db] = mfma32(fo.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+          fence_every<2>(db);
         }
         if constexpr (ATOMIC) {
+          if (!CAUSAL && key >= N) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              sb0[e] = (__bf16)0.f;
+              sb1[e] = (__bf16)0.f;
+            }
+          }
           *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 8 * g)) = sb0;
           *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = sb1;
         }
@@ -272,27 +207,136 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
     }
     if constexpr (ATOMIC) {
       __syncthreads();
-      float* dqh = a.dq + head;
       for (int t = wave; t < QBN * DB; t += NW) {
         const int qb = t / DB, db = t % DB;
         f32x16 acc = zero16();
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-          acc = mfma32(col_frag<BQ>(dst, ks * 16, qb * 32, lane), col_frag<D>(ktile, ks * 16, db * 32, lane), acc);
+          acc = mfma32(FragOffsets<BQ>::col_dyn(dst, ks * 16, qb, lane), FragOffsets<D>::col_dyn(ktile, ks * 16, db, lane),
+                       acc);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * a.scale);
+          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
         }
       }
     }
-    if (more) {
-      LDS char* nxt = smem + (buf ^ 1) * STAGE;
-      sq.store(nxt, tid);
-      sdo.store(nxt + QTILE, tid);
-      srow.store((LDS float*)(nxt + 2 * QTILE), tid);
+  }
+};
+
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS>
+__global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
+  using M = DkdvMath<D, BQ, NW, CAUSAL, ATOMIC, KV_LDS>;
+  constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
+  constexpr int NT = NW * 64;
+  constexpr int QTILE = BQ * D * 2;
+  constexpr int KT_BYTES = (ATOMIC || KV_LDS) ? BK * D * 2 : 16;
+  constexpr int VT_BYTES = KV_LDS ? BK * D * 2 : 16;
+  constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 16;
+  __shared__ __attribute__((aligned(1024))) char q0s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char d0s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char q1s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char d1s[QTILE];
+  __shared__ __attribute__((aligned(16))) float st0s[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float st1s[2 * BQ];
+  __shared__ __attribute__((aligned(1024))) char kts[KT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vts[VT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsts[DST_BYTES];
+  LDS char* qbuf0 = (LDS char*)q0s;
+  LDS char* dbuf0 = (LDS char*)d0s;
+  LDS char* qbuf1 = (LDS char*)q1s;
+  LDS char* dbuf1 = (LDS char*)d1s;
+  LDS float* st0 = (LDS float*)st0s;
+  LDS float* st1 = (LDS float*)st1s;
+  LDS char* ktile = (LDS char*)kts;
+  LDS char* vtile = (LDS char*)vts;
+  LDS char* dst = (LDS char*)dsts;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int N = a.N;
+  const int nkt = (N + BK - 1) / BK;
+  int bh, kt;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, a.B * a.H, nkt, false, bh, kt);  // low key tiles see the most queries
+  } else {
+    const int item = xcd_remap(blockIdx.x, a.B * a.H * nkt);
+    bh = item / nkt;
+    kt = item % nkt;
+  }
+  const size_t head = (size_t)bh * N * D;
+  const __bf16* Qh = a.q + head;
+  const __bf16* Kh = a.k + head;
+  const __bf16* Vh = a.v + head;
+  const __bf16* dOh = a.dout + head;
+  const float* lseh = a.lse + (size_t)bh * N;
+  const float* delh = a.delta + (size_t)bh * N;
+  float* dqh = ATOMIC ? a.dq + head : nullptr;
+  const float c = a.scale * kLog2e;
+
+  const int k0 = kt * BK;
+  const int kw = k0 + wave * 32;
+  const int key = kw + l32;
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  using QDMA = TileDMA<BQ, D, NW>;
+
+  QDMA::issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
+  QDMA::issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
+  if constexpr (ATOMIC || KV_LDS) TileDMA<BK, D, NW>::issue(Kh, k0, N, ktile, wave, lane);
+  if constexpr (KV_LDS) TileDMA<BK, D, NW>::issue(Vh, k0, N, vtile, wave, lane);
+  RowStager<BQ, NT> srow;
+  srow.load(lseh, delh, qt0 * BQ, N, tid);
+  srow.store(st0, tid);
+
+  bf16x8 kf[KV_LDS ? 1 : KK], vf[KV_LDS ? 1 : KK];
+  if constexpr (!KV_LDS) {
+    const int krow_g = min(key, N - 1);  // keys past the end are masked (P = 0) and never stored
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kf[kk] = *(const bf16x8*)(Kh + (size_t)krow_g * D + kk * 16 + g * 8);
+      vf[kk] = *(const bf16x8*)(Vh + (size_t)krow_g * D + kk * 16 + g * 8);
     }
+  }
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+  FragOffsets<D> fo;
+  fo.init(lane);
+  PlainRowOffsets<D> po;
+  if constexpr (KV_LDS) po.init(lane);
+
+  wait_tile();
+  __syncthreads();
+  for (int it = qt0; it < nqt; it += 2) {
+    fo.refresh();
+    if constexpr (KV_LDS) po.refresh();
+    if (it + 1 < nqt) {
+      QDMA::issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
+      QDMA::issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
+      srow.load(lseh, delh, (it + 1) * BQ, N, tid);
+    }
+    M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fo, po,
+            wave, g, l32, lane);
+    if (it + 1 < nqt) srow.store(st1, tid);
+    wait_tile();
+    __syncthreads();
+    if (it + 1 >= nqt) break;
+    fo.refresh();
+    if constexpr (KV_LDS) po.refresh();
+    if (it + 2 < nqt) {
+      QDMA::issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
+      QDMA::issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
+      srow.load(lseh, delh, (it + 2) * BQ, N, tid);
+    }
+    M::tile(qbuf1, dbuf1, st1, ktile, vtile, dst, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N, c, a.scale,
+            fo, po, wave, g, l32, lane);
+    if (it + 2 < nqt) srow.store(st0, tid);
+    wait_tile();
     __syncthreads();
   }
 
@@ -317,31 +361,80 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dQ kernel of the 7-GEMM design: one workgroup owns BR = 32 * NW queries, each
 // wave 32 (one per lane column), and walks the key/value tiles in the forward's
-// direction.  Per tile:
+// direction, the tiles arriving by direct-to-LDS loads one tile ahead.  Per tile:
 //   S^T = K Q^T,  dP^T = V dO^T     A = K / V row fragments (LDS), B = Q^T / dO^T
 //   P^T, dS^T                        one lse and one delta per lane
 //   dQ^T += K^T dS^T                 A = transposed reads of the K tile
 // No atomics: each dq element is written once, so results are reproducible bit
-// for bit ("Potential algorithmic improvements...": the 7-GEMM form is
-// deterministic).
-template <int D, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
+// for bit (issue 1172: the 7-GEMM form is deterministic).
+template <int D, int BC, bool CAUSAL>
+struct DqMath {
+  static constexpr int KB = BC / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int KK = D / 16;
+  __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
+                                              const bf16x8 (&dof)[KK], f32x16 (&dq)[DB], float lse2, float dl,
+                                              int k0, int q_w, int qi, int N, float c, const FragOffsets<D>& fo,
+                                              int g) {
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w);
+    bf16x8 dsb[2 * KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        s = mfma32(fo.row(kt, kb * 32, kk), qf[kk], s);
+        dp = mfma32(fo.row(vt, kb * 32, kk), dof[kk], dp);
+        fence_every<4>(kk);
+      }
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_hw(fmaf(s[r], c, -lse2));
+        if (need_mask) {
+          const int kidx = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (kidx >= N || (CAUSAL && kidx > qi)) pv = 0.f;
+        }
+        ds[r] = pv * (dp[r] - dl);
+      }
+      dsb[2 * kb] = pack8(ds, 0);
+      dsb[2 * kb + 1] = pack8(ds, 8);
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks) dq[db] = mfma32(fo.col(kt, ks * 16, db), dsb[ks], dq[db]);
+    }
+  }
+};
+
+template <int D, int BC, int NW, int OCC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
+  using M = DqMath<D, BC, CAUSAL>;
   constexpr int BR = 32 * NW;
-  constexpr int NT = NW * 64;
   constexpr int TILE = BC * D * 2;
-  constexpr int KB = BC / 32;
-  constexpr int DB = D / 32;
-  constexpr int KK = D / 16;
-  __shared__ __attribute__((aligned(1024))) char smem_raw[4 * TILE];
-  LDS char* smem = (LDS char*)smem_raw;
+  constexpr int DB = M::DB, KK = M::KK;
+  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+  LDS char* kbuf0 = (LDS char*)k0s;
+  LDS char* vbuf0 = (LDS char*)v0s;
+  LDS char* kbuf1 = (LDS char*)k1s;
+  LDS char* vbuf1 = (LDS char*)v1s;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BR - 1) / BR;
-  const int item = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = item / nqt;
-  const int qt = CAUSAL ? nqt - 1 - item % nqt : item % nqt;
+  int bh, qt;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, a.B * a.H, nqt, true, bh, qt);
+  } else {
+    const int item = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+    bh = item / nqt;
+    qt = item % nqt;
+  }
   const size_t head = (size_t)bh * N * D;
   const __bf16* Qh = a.q + head;
   const __bf16* Kh = a.k + head;
@@ -352,89 +445,51 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
   const int q_wg = qt * BR;
   const int q_w = q_wg + wave * 32;
   const int qi = q_w + l32;
-
-  bf16x8 qf[KK], dof[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    if (qi < N) {
-      qf[kk] = *(const bf16x8*)(Qh + (size_t)qi * D + kk * 16 + g * 8);
-      dof[kk] = *(const bf16x8*)(dOh + (size_t)qi * D + kk * 16 + g * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qf[kk][e] = (__bf16)0.f;
-        dof[kk][e] = (__bf16)0.f;
-      }
-    }
-  }
-  const float lse2 = qi < N ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
-  const float dl = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
-
-  f32x16 dq[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) dq[db] = zero16();
-
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
-  const int krow = pi_row(l32);
+  using DMA = TileDMA<BC, D, NW>;
 
-  TileStager<BC, D, NT> sk, sv;
-  sk.load(Kh, 0, N, tid);
-  sv.load(Vh, 0, N, tid);
-  sk.store(smem, tid);
-  sv.store(smem + TILE, tid);
+  DMA::issue(Kh, 0, N, kbuf0, wave, lane);
+  DMA::issue(Vh, 0, N, vbuf0, wave, lane);
+
+  const int qrow = min(qi, N - 1);  // rows past the end get lse = +inf (P = 0) and are never stored
+  bf16x8 qf[KK], dof[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = *(const bf16x8*)(Qh + (size_t)qrow * D + kk * 16 + g * 8);
+    dof[kk] = *(const bf16x8*)(dOh + (size_t)qrow * D + kk * 16 + g * 8);
+  }
+  const float lse2 = qi < N ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
+  const float dl = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = zero16();
+  FragOffsets<D> fo;
+  fo.init(lane);
+
+  wait_tile();
   __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const LDS char* kt = smem + (j & 1) * 2 * TILE;
-    const LDS char* vt = kt + TILE;
-    const bool more = j + 1 < nkt;
-    if (more) {
-      sk.load(Kh, (j + 1) * BC, N, tid);
-      sv.load(Vh, (j + 1) * BC, N, tid);
+  for (int j = 0; j < nkt; j += 2) {
+    fo.refresh();
+    if (j + 1 < nkt) {
+      DMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      DMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
-    const int k0 = j * BC;
-    const bool active = !CAUSAL || k0 <= q_w + 31;
-    if (active) {
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w);
-      bf16x8 dsb[2 * KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 ka = row_frag<D>(kt, kb * 32 + krow, kk * 16 + g * 8);
-          const bf16x8 va = row_frag<D>(vt, kb * 32 + krow, kk * 16 + g * 8);
-          s = mfma32(ka, qf[kk], s);
-          dp = mfma32(va, dof[kk], dp);
-        }
-        f32x16 ds;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_hw(fmaf(s[r], c, -lse2));
-          if (need_mask) {
-            const int kidx = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-            if (kidx >= N || (CAUSAL && kidx > qi)) pv = 0.f;
-          }
-          ds[r] = pv * (dp[r] - dl);
-        }
-        dsb[2 * kb] = pack8(ds, 0);
-        dsb[2 * kb + 1] = pack8(ds, 8);
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int ks = 0; ks < 2 * KB; ++ks) {
-          dq[db] = mfma32(col_frag<D>(kt, ks * 16, db * 32, lane), dsb[ks], dq[db]);
-        }
-      }
+    // waves wholly past the end (padding rows) or below this key tile's diagonal skip the tile
+    if (q_w < N && (!CAUSAL || j * BC <= q_w + 31))
+      M::step(kbuf0, vbuf0, qf, dof, dq, lse2, dl, j * BC, q_w, qi, N, c, fo, g);
+    wait_tile();
+    __syncthreads();
+    if (j + 1 >= nkt) break;
+    fo.refresh();
+    if (j + 2 < nkt) {
+      DMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      DMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
-    if (more) {
-      LDS char* nt = smem + ((j + 1) & 1) * 2 * TILE;
-      sk.store(nt, tid);
-      sv.store(nt + TILE, tid);
-    }
+    if (q_w < N && (!CAUSAL || (j + 1) * BC <= q_w + 31))
+      M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fo, g);
+    wait_tile();
     __syncthreads();
   }
 
@@ -469,16 +524,16 @@ static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   return 0;
 }
 
-template <int D, int BC, int NW>
+template <int D, int BC, int NW, int OCC>
 static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.H * nqt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   }
   return 0;
 }
@@ -487,13 +542,14 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, false, KVL> }
 #define DKDVA_CFG(D, BQ, NW, KVL) \
   { D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, true, KVL> }
-#define DQ_CFG(D, BC, NW) \
-  { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC, &launch_dq<D, BC, NW> }
+#define DQ_CFG(D, BC, NW, OCC) \
+  { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC> }
 
 const BwdConfig* dkdv_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDV_CFG(64, 32, 4, false),  DKDV_CFG(64, 64, 4, false),
-      DKDV_CFG(128, 32, 4, false), DKDV_CFG(128, 64, 4, false),
+      DKDV_CFG(64, 64, 4, false),  DKDV_CFG(64, 32, 4, false),  DKDV_CFG(64, 64, 8, false),
+      DKDV_CFG(128, 64, 4, false), DKDV_CFG(128, 32, 4, false), DKDV_CFG(128, 32, 4, true),
+      DKDV_CFG(128, 64, 4, true),  DKDV_CFG(128, 32, 2, true),
       DKDV_CFG(256, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
@@ -502,8 +558,8 @@ const BwdConfig* dkdv_configs(int* count) {
 
 const BwdConfig* dkdv_atomic_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDVA_CFG(64, 32, 4, false), DKDVA_CFG(64, 64, 4, false),
-      DKDVA_CFG(128, 32, 4, false), DKDVA_CFG(128, 64, 4, false),
+      DKDVA_CFG(64, 64, 4, false),  DKDVA_CFG(64, 32, 4, false),  DKDVA_CFG(64, 64, 8, false),
+      DKDVA_CFG(128, 64, 4, false), DKDVA_CFG(128, 32, 4, false),
       DKDVA_CFG(256, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
@@ -512,9 +568,9 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
 
 const BwdConfig* dq_configs(int* count) {
   static const BwdConfig table[] = {
-      DQ_CFG(64, 64, 4),  DQ_CFG(64, 128, 4),
-      DQ_CFG(128, 32, 4), DQ_CFG(128, 64, 4),
-      DQ_CFG(256, 32, 4),
+      DQ_CFG(64, 64, 4, 2),  DQ_CFG(64, 128, 4, 2), DQ_CFG(64, 64, 8, 2),
+      DQ_CFG(128, 64, 4, 2), DQ_CFG(128, 32, 4, 2), DQ_CFG(128, 64, 8, 2),
+      DQ_CFG(256, 32, 4, 1), DQ_CFG(256, 64, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -62,11 +62,13 @@ __device__ __forceinline__ int pi_row(int R) {
 // swz = 4 (r % 4) ^ 2 ((r / 8) % 2) puts the 4 consecutive rows of a transposed
 // read in 4 different 64-byte quarters and the 8 rows of a row-fragment group on 8
 // different 16-byte bank groups.  (W = 64 packs two rows per 256-byte bank line
-// and uses the analogous bits; W = 32 is only read transposed.)
+// and uses the analogous bits; W = 32 is only read transposed.)  Every variant
+// satisfies swz(r + 4) == swz(r) for r % 8 < 4: a transposed fragment's second
+// read (4 rows further down) reuses the first read's lane offset.
 template <int W>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (W == 32) {
-    return ((row >> 2) & 1) << 1;
+    return ((row >> 3) & 1) << 1;
   } else if constexpr (W == 64) {
     return (((row >> 1) & 1) << 2) ^ (((row >> 3) & 1) << 1);
   } else {
@@ -99,6 +101,81 @@ __device__ __forceinline__ bf16x8 col_frag(const LDS char* tile, int r0, int c0,
   const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// Per-lane LDS byte offsets for the fragment reads of a W-wide swizzled tile.
+// Row fragments read rows R + pi(l % 32) (R a multiple of 32) at chunk 2 kk + l / 32;
+// transposed reads read rows r0 + 8 (l / 32) + (l % 16) / 4 (+4), r0 a multiple of
+// 16, at columns 32 db + 16 ((l / 16) % 2) + 4 (l % 4).  The swizzle only depends on
+// the row's low bits, so one register per chunk pattern covers every R / r0: the
+// row base and the chunk-pair above 16 (for W = 256) become compile-time constants
+// that fold into the ds_read immediate.  refresh() hides the values from loop-
+// invariant hoisting, which would otherwise materialise (and spill) one register
+// per (buffer, row, chunk) combination.
+template <int W>
+struct FragOffsets {
+  static constexpr int NR = (W / 16) < 8 ? (W / 16) : 8;
+  static constexpr int NC = (W / 32) < 4 ? (W / 32) : 4;
+  int rf[NR];
+  int cf[NC];
+  __device__ __forceinline__ void init(int lane) {
+    const int g = lane >> 5;
+    const int rrow = pi_row(lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < NR; ++kk) rf[kk] = tile_off<W>(rrow, kk * 16 + g * 8);
+    const int crow = ((lane >> 5) << 3) + ((lane & 15) >> 2);
+    const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+#pragma unroll
+    for (int db = 0; db < NC; ++db) cf[db] = tile_off<W>(crow, db * 32 + ccol);
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(rf[i]));
+#pragma unroll
+    for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(cf[i]));
+  }
+  // Row fragment: rows R + pi(l % 32), elements 16 kk + 8 (l / 32) .. +7.
+  __device__ __forceinline__ bf16x8 row(const LDS char* tile, int R, int kk) const {
+    return *(const LDS bf16x8*)(tile + R * (2 * W) + (kk / NR) * 256 + rf[kk % NR]);
+  }
+  // Transposed fragment for a run-time db (computes the lane offset instead of
+  // indexing the register array, which would force it into scratch memory).
+  __device__ __forceinline__ static bf16x8 col_dyn(const LDS char* tile, int r0, int db, int lane) {
+    const int crow = ((lane >> 5) << 3) + ((lane & 15) >> 2);
+    const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+    const LDS char* p = tile + r0 * (2 * W) + tile_off<W>(crow, db * 32 + ccol);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p + 4 * (2 * W)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+  // Transposed fragment: lane l gets tile[r0 + 8 (l / 32) + e][32 db + l % 32], e = 0..7.
+  __device__ __forceinline__ bf16x8 col(const LDS char* tile, int r0, int db) const {
+    const LDS char* p = tile + r0 * (2 * W) + (db / NC) * 256 + cf[db % NC];
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p + 4 * (2 * W)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+};
+
+// Row fragments of rows R + l % 32 (plain order; the B operand of a product whose
+// contraction runs along the row, one row per lane column).
+template <int W>
+struct PlainRowOffsets {
+  static constexpr int NR = (W / 16) < 8 ? (W / 16) : 8;
+  int rf[NR];
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int kk = 0; kk < NR; ++kk) rf[kk] = tile_off<W>(lane & 31, kk * 16 + (lane >> 5) * 8);
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(rf[i]));
+  }
+  __device__ __forceinline__ bf16x8 row(const LDS char* tile, int R, int kk) const {
+    return *(const LDS bf16x8*)(tile + R * (2 * W) + (kk / NR) * 256 + rf[kk % NR]);
+  }
+};
 
 // Register-staged copy of a ROWS x W bf16 tile from global memory (rows of pitch
 // W elements, rows >= valid_rows read as zeros) into the swizzled LDS layout.
@@ -162,6 +239,13 @@ struct TileDMA {
 
 __device__ __forceinline__ void wait_tile() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Scheduling fence every CH iterations of an unrolled loop: bounds how many LDS
+// fragment reads the scheduler hoists ahead of their MFMAs (each costs 4 VGPRs).
+template <int CH>
+__device__ __forceinline__ void fence_every(int i) {
+  if (((i + 1) % CH) == 0) __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // Reductions across the two 32-lane halves (lane l and lane l ^ 32), which hold
 // the two halves of a 32-key (or 32-query) block in the C layout.
@@ -207,6 +291,25 @@ __device__ __forceinline__ int xcd_remap(int x, int total) {
   const int q = total >> 3, r = total & 7;
   const int xcd = x & 7, local = x >> 3;
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+}
+
+// Causal work order.  Tile costs differ (a query tile late in the sequence sees
+// many keys; a key tile early in the sequence is seen by many queries), so the
+// heaviest tiles are dispatched first.  With B*H a multiple of 8, XCD x (the one
+// receiving workgroups x, x + 8, ...) keeps the heads h = x (mod 8) and walks
+// them rank by rank, heaviest rank first; otherwise the order is rank-major over
+// all heads.  heavy_high: the heaviest tile has the largest index.
+__device__ __forceinline__ void causal_order(int x, int BH, int ntiles, bool heavy_high, int& bh, int& tile) {
+  int rank;
+  if ((BH & 7) == 0) {
+    const int hp = BH >> 3, u = x >> 3;
+    rank = u / hp;
+    bh = (x & 7) + 8 * (u % hp);
+  } else {
+    rank = x / BH;
+    bh = x % BH;
+  }
+  tile = heavy_high ? ntiles - 1 - rank : rank;
 }
 
 }  // namespace fa

@@ -40,13 +40,13 @@ struct FwdTileMath {
   // One K/V tile for one wave: 32 queries (one per lane column) x BC keys.
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               f32x16 (&o)[DB], float& m_run, float& l_run, float& lb_run, int k0,
-                                              int q_w, int qi, int N, float c, int krow, int g, int lane) {
+                                              int q_w, int qi, int N, float c, const FragOffsets<D>& fo, int g) {
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(row_frag<D>(kt, kb * 32 + krow, kk * 16 + g * 8), qf[kk], s[kb]);
+      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(fo.row(kt, kb * 32, kk), qf[kk], s[kb]);
     }
     // keys past the end, and (causal) keys after the query, score -inf
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w)) {
@@ -101,7 +101,7 @@ struct FwdTileMath {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(col_frag<D>(vt, ks * 16, db * 32, lane), pb[ks], o[db]);
+      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(fo.col(vt, ks * 16, db), pb[ks], o[db]);
     }
   }
 };
@@ -127,9 +127,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const int g = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BR - 1) / BR;
-  const int item = xcd_remap(blockIdx.x, a.B * a.H * nqt);
-  const int bh = item / nqt;
-  const int qt = CAUSAL ? nqt - 1 - item % nqt : item % nqt;  // causal: heavy tiles first
+  int bh, qt;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, a.B * a.H, nqt, true, bh, qt);
+  } else {
+    const int item = xcd_remap(blockIdx.x, a.B * a.H * nqt);
+    bh = item / nqt;
+    qt = item % nqt;
+  }
   const size_t head = (size_t)bh * N * D;
   const __bf16* Qh = a.q + head;
   const __bf16* Kh = a.k + head;
@@ -156,26 +161,29 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
-  const int krow = pi_row(l32);
+  FragOffsets<D> fo;
+  fo.init(lane);
 
   wait_tile();
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
+    fo.refresh();
     if (j + 1 < nkt) {
       DMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
       DMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     if (!CAUSAL || j * BC <= q_w + 31)
-      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, krow, g, lane);
+      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fo, g);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
+    fo.refresh();
     if (j + 2 < nkt) {
       DMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
       DMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (!CAUSAL || (j + 1) * BC <= q_w + 31)
-      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, krow, g, lane);
+      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fo, g);
     wait_tile();
     __syncthreads();
   }

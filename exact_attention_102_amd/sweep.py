@@ -1,0 +1,99 @@
+"""Block-shape sweep: times every tile configuration of every kernel on one workload.
+
+    python -m exact_attention_102_amd.sweep --workload b4_h16_n2048_d128 [--causal 0|1] [--out file.jsonl]
+
+"Potential algorithmic improvements for backward pass" (flash-attention issue 1172)
+treats the block shape -- rows owned per workgroup x rows walked per tile, and
+what stays in registers -- as a search under register pressure, with non-square
+shapes such as 32-64 x 160-320.  This tool measures each compiled configuration
+(fa_num_configs / fa_config_name) with the same protocol as that page's benchmark
+(5 trials of 5 back-to-back dispatches; best and median reported) and prints one
+JSON record per (pass, configuration); the library's default table is set from
+these results.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def time_calls(fn, torch, trials=5, dispatches=5, warmup=2):
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(dispatches):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) / dispatches)
+    per.sort()
+    return per[0], per[len(per) // 2]
+
+
+def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3)):
+    import torch
+
+    import workloads
+    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_config_name,
+                                         fa_default_config, fa_fwd, fa_num_configs)
+    from exact_attention_102_amd.flops import attention_flops
+
+    w = workloads.WORKLOADS[workload]
+    causal = w.causal if causal_override is None else bool(causal_override)
+    B, H, N, d = w.B, w.H, w.N, w.d
+    q, k, v, do = (workloads.to_bf16(x).cuda() for x in workloads.draw_workload(w))
+    f32 = dict(dtype=torch.float32, device="cuda")
+    o = torch.empty((B, H, N, d), **f32)
+    lse = torch.empty((B, H, N), **f32)
+    delta = torch.empty((B, H, N), **f32)
+    dq, dk, dv = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+    fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse)
+    fa_bwd_preprocess(o, do, delta=delta)
+    fl = attention_flops(B, H, N, d, causal)
+    p = fl["pairs"]
+    gemms = {0: 2, 1: 4, 2: 5, 3: 3}
+    out = []
+    for pass_id in passes:
+        for cfg in range(fa_num_configs(pass_id, d)):
+            if pass_id == 0:
+                fn = lambda: fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, cfg=cfg)
+            elif pass_id in (1, 2):
+                atomic = pass_id == 2
+                fn = lambda: fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, atomic, dk, dv, dq=dq, cfg=cfg)
+            else:
+                fn = lambda: fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq, cfg=cfg)
+            best, med = time_calls(fn, torch)
+            flops = 2 * gemms[pass_id] * d * p
+            rec = {"workload": w.name, "causal": causal, "pass": ["fwd", "dkdv", "dkdv_atomic", "dq"][pass_id],
+                   "cfg": cfg, "name": fa_config_name(pass_id, d, causal, cfg),
+                   "default": cfg == fa_default_config(pass_id, d, causal),
+                   "best_ms": round(best, 4), "median_ms": round(med, 4),
+                   "tflops_best": round(flops / best / 1e9, 1), "tflops_median": round(flops / med / 1e9, 1)}
+            print(json.dumps(rec), flush=True)
+            out.append(rec)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--workload", default="b4_h16_n2048_d128")
+    ap.add_argument("--causal", type=int, default=-1)
+    ap.add_argument("--passes", default="0,1,2,3")
+    args = ap.parse_args()
+    sweep(args.workload, None if args.causal < 0 else args.causal, tuple(int(x) for x in args.passes.split(",")))
+
+
+if __name__ == "__main__":
+    main()
