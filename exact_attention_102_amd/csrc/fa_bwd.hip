@@ -105,6 +105,8 @@ struct RowStager {
 // KV_LDS keeps the workgroup's K and V in LDS instead of registers (large d).
 template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS>
 struct DkdvMath {
+  // K tile: plain row fragments (KV_LDS) and/or transposed reads (atomic dQ product)
+  static constexpr int KMODE = ATOMIC ? (KV_LDS ? kBoth : kColOnly) : kRowOnly;
   static constexpr int BK = 32 * NW;
   static constexpr int QBN = BQ / 32;
   static constexpr int DB = D / 32;
@@ -114,8 +116,10 @@ struct DkdvMath {
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
                                               const bf16x8* kf, const bf16x8* vf, f32x16 (&dk)[DB],
                                               f32x16 (&dv)[DB], float* dqh, int q0, int k0, int kw, int key, int N,
-                                              float c, float scale, const FragOffsets<D>& fo,
-                                              const PlainRowOffsets<D>& po, int wave, int g, int l32, int lane) {
+                                              float c, float scale, const RowOffsets<D, kBoth>& fr,
+                                              const ColOffsets<D, kBoth>& fc, const RowOffsets<D, KMODE>& pk,
+                                              const RowOffsets<D, kRowOnly>& pv, int wave, int g, int l32,
+                                              int lane) {
     const LDS float* l2t = stats;
     const LDS float* dlt = stats + BQ;
 #pragma unroll
@@ -132,14 +136,14 @@ struct DkdvMath {
         for (int kk = 0; kk < KK; ++kk) {
           bf16x8 kb, vb;
           if constexpr (KV_LDS) {
-            kb = po.row(ktile, wave * 32, kk);
-            vb = po.row(vtile, wave * 32, kk);
+            kb = pk.row(ktile, wave * 32, kk);
+            vb = pv.row(vtile, wave * 32, kk);
           } else {
             kb = kf[kk];
             vb = vf[kk];
           }
-          s = mfma32(fo.row(qtl, qb * 32, kk), kb, s);
-          dp = mfma32(fo.row(dotl, qb * 32, kk), vb, dp);
+          s = mfma32(fr.row(qtl, qb * 32, kk), kb, s);
+          dp = mfma32(fr.row(dotl, qb * 32, kk), vb, dp);
           fence_every<4>(kk);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -180,10 +184,10 @@ struct DkdvMath {
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(fo.col(dotl, qb * 32, db), pb0, dv[db]);
-          dv[db] = mfma32(fo.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
-          dk[db] = mfma32(fo.col(qtl, qb * 32, db), sb0, dk[db]);
-          dk[db] = mfma32(fo.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+          dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
+          dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+          dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
+          dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
           fence_every<2>(db);
         }
         if constexpr (ATOMIC) {
@@ -194,15 +198,15 @@ struct DkdvMath {
               sb1[e] = (__bf16)0.f;
             }
           }
-          *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 8 * g)) = sb0;
-          *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = sb1;
+          *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 8 * g)) = sb0;
+          *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = sb1;
         }
       } else if constexpr (ATOMIC) {
         bf16x8 z;
 #pragma unroll
         for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
-        *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 8 * g)) = z;
-        *(LDS bf16x8*)(dst + tile_off<BQ>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = z;
+        *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 8 * g)) = z;
+        *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = z;
       }
     }
     if constexpr (ATOMIC) {
@@ -212,8 +216,8 @@ struct DkdvMath {
         f32x16 acc = zero16();
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-          acc = mfma32(FragOffsets<BQ>::col_dyn(dst, ks * 16, qb, lane), FragOffsets<D>::col_dyn(ktile, ks * 16, db, lane),
-                       acc);
+          acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
+                       ColOffsets<D, KMODE>::col_dyn(ktile, ks * 16, db, lane), acc);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -280,12 +284,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const int key = kw + l32;
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
-  using QDMA = TileDMA<BQ, D, NW>;
+  using QDMA = TileDMA<BQ, D, NW, kBoth>;  // Q, dO: row fragments and transposed reads
+  constexpr int KMODE = M::KMODE;
 
   QDMA::issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
   QDMA::issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
-  if constexpr (ATOMIC || KV_LDS) TileDMA<BK, D, NW>::issue(Kh, k0, N, ktile, wave, lane);
-  if constexpr (KV_LDS) TileDMA<BK, D, NW>::issue(Vh, k0, N, vtile, wave, lane);
+  if constexpr (ATOMIC || KV_LDS) TileDMA<BK, D, NW, KMODE>::issue(Kh, k0, N, ktile, wave, lane);
+  if constexpr (KV_LDS) TileDMA<BK, D, NW, kRowOnly>::issue(Vh, k0, N, vtile, wave, lane);
   RowStager<BQ, NT> srow;
   srow.load(lseh, delh, qt0 * BQ, N, tid);
   srow.store(st0, tid);
@@ -305,36 +310,50 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     dk[db] = zero16();
     dv[db] = zero16();
   }
-  FragOffsets<D> fo;
-  fo.init(lane);
-  PlainRowOffsets<D> po;
-  if constexpr (KV_LDS) po.init(lane);
+  RowOffsets<D, kBoth> fr;
+  fr.init(lane);
+  ColOffsets<D, kBoth> fc;
+  fc.init(lane);
+  RowOffsets<D, KMODE> pk;
+  RowOffsets<D, kRowOnly> pv;
+  if constexpr (KV_LDS) {
+    pk.init(lane, true);
+    pv.init(lane, true);
+  }
 
   wait_tile();
   __syncthreads();
   for (int it = qt0; it < nqt; it += 2) {
-    fo.refresh();
-    if constexpr (KV_LDS) po.refresh();
+    fr.refresh();
+    fc.refresh();
+    if constexpr (KV_LDS) {
+      pk.refresh();
+      pv.refresh();
+    }
     if (it + 1 < nqt) {
       QDMA::issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
       QDMA::issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
       srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
-    M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fo, po,
-            wave, g, l32, lane);
+    M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
+            pk, pv, wave, g, l32, lane);
     if (it + 1 < nqt) srow.store(st1, tid);
     wait_tile();
     __syncthreads();
     if (it + 1 >= nqt) break;
-    fo.refresh();
-    if constexpr (KV_LDS) po.refresh();
+    fr.refresh();
+    fc.refresh();
+    if constexpr (KV_LDS) {
+      pk.refresh();
+      pv.refresh();
+    }
     if (it + 2 < nqt) {
       QDMA::issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
       QDMA::issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
       srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, dst, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N, c, a.scale,
-            fo, po, wave, g, l32, lane);
+            fr, fc, pk, pv, wave, g, l32, lane);
     if (it + 2 < nqt) srow.store(st0, tid);
     wait_tile();
     __syncthreads();
@@ -374,8 +393,9 @@ struct DqMath {
   static constexpr int KK = D / 16;
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               const bf16x8 (&dof)[KK], f32x16 (&dq)[DB], float lse2, float dl,
-                                              int k0, int q_w, int qi, int N, float c, const FragOffsets<D>& fo,
-                                              int g) {
+                                              int k0, int q_w, int qi, int N, float c,
+                                              const RowOffsets<D, kBoth>& fkr, const ColOffsets<D, kBoth>& fkc,
+                                              const RowOffsets<D, kRowOnly>& fvr, int g) {
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w);
     bf16x8 dsb[2 * KB];
 #pragma unroll
@@ -383,8 +403,8 @@ struct DqMath {
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s = mfma32(fo.row(kt, kb * 32, kk), qf[kk], s);
-        dp = mfma32(fo.row(vt, kb * 32, kk), dof[kk], dp);
+        s = mfma32(fkr.row(kt, kb * 32, kk), qf[kk], s);
+        dp = mfma32(fvr.row(vt, kb * 32, kk), dof[kk], dp);
         fence_every<4>(kk);
       }
       f32x16 ds;
@@ -403,7 +423,7 @@ struct DqMath {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) dq[db] = mfma32(fo.col(kt, ks * 16, db), dsb[ks], dq[db]);
+      for (int ks = 0; ks < 2 * KB; ++ks) dq[db] = mfma32(fkc.col(kt, ks * 16, db), dsb[ks], dq[db]);
     }
   }
 };
@@ -448,10 +468,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
-  using DMA = TileDMA<BC, D, NW>;
+  using KDMA = TileDMA<BC, D, NW, kBoth>;     // K: row fragments and transposed reads
+  using VDMA = TileDMA<BC, D, NW, kRowOnly>;  // V: row fragments only
 
-  DMA::issue(Kh, 0, N, kbuf0, wave, lane);
-  DMA::issue(Vh, 0, N, vbuf0, wave, lane);
+  KDMA::issue(Kh, 0, N, kbuf0, wave, lane);
+  VDMA::issue(Vh, 0, N, vbuf0, wave, lane);
 
   const int qrow = min(qi, N - 1);  // rows past the end get lse = +inf (P = 0) and are never stored
   bf16x8 qf[KK], dof[KK];
@@ -465,30 +486,38 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = zero16();
-  FragOffsets<D> fo;
-  fo.init(lane);
+  RowOffsets<D, kBoth> fkr;
+  fkr.init(lane);
+  ColOffsets<D, kBoth> fkc;
+  fkc.init(lane);
+  RowOffsets<D, kRowOnly> fvr;
+  fvr.init(lane);
 
   wait_tile();
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
-    fo.refresh();
+    fkr.refresh();
+    fkc.refresh();
+    fvr.refresh();
     if (j + 1 < nkt) {
-      DMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
-      DMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
+      KDMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      VDMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     // waves wholly past the end (padding rows) or below this key tile's diagonal skip the tile
     if (q_w < N && (!CAUSAL || j * BC <= q_w + 31))
-      M::step(kbuf0, vbuf0, qf, dof, dq, lse2, dl, j * BC, q_w, qi, N, c, fo, g);
+      M::step(kbuf0, vbuf0, qf, dof, dq, lse2, dl, j * BC, q_w, qi, N, c, fkr, fkc, fvr, g);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
-    fo.refresh();
+    fkr.refresh();
+    fkc.refresh();
+    fvr.refresh();
     if (j + 2 < nkt) {
-      DMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
-      DMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
+      KDMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      VDMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (q_w < N && (!CAUSAL || (j + 1) * BC <= q_w + 31))
-      M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fo, g);
+      M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fkr, fkc, fvr, g);
     wait_tile();
     __syncthreads();
   }

@@ -50,162 +50,108 @@ __device__ __forceinline__ int pi_row(int R) {
 }
 
 // ---------------------------------------------------------------------------
-// Swizzled LDS tile of bf16, W elements per row (row pitch 2W bytes, no padding).
+// Swizzled LDS tiles of bf16, W elements per row (row pitch 2W bytes, no padding).
 // The 16-byte chunk c of row r is stored at chunk position c ^ swz(r).  Two read
-// shapes must both avoid LDS bank conflicts (64 banks of 4 bytes):
-//  * row fragments (ds_read_b128): each group of 8 lanes reads the same chunk of
-//    8 distinct rows {R..R+3, R+8..R+11};
+// shapes exist (64 banks of 4 bytes):
+//  * row fragments (ds_read_b128): 16 lanes read the same chunk of 16 distinct rows;
 //  * transposed reads (ds_read_b64_tr_b16): 16 lanes read 4 consecutive rows x 32
 //    contiguous bytes, a half-wave 4 rows x 64 bytes.  Measured on gfx950, these
 //    slow down when the XOR flips the lowest chunk bit (it reorders the two 16-byte
-//    halves of a 32-byte row segment), so the swizzle only touches bits 1..3.
-// swz = 4 (r % 4) ^ 2 ((r / 8) % 2) puts the 4 consecutive rows of a transposed
-// read in 4 different 64-byte quarters and the 8 rows of a row-fragment group on 8
-// different 16-byte bank groups.  (W = 64 packs two rows per 256-byte bank line
-// and uses the analogous bits; W = 32 is only read transposed.)  Every variant
-// satisfies swz(r + 4) == swz(r) for r % 8 < 4: a transposed fragment's second
-// read (4 rows further down) reuses the first read's lane offset.
-template <int W>
+//    halves of a 32-byte row segment).
+// A tile read only one way gets the best swizzle for that shape; a tile read both
+// ways gets a compromise (all measured with MFMA-fed read loops):
+//  kRowOnly  swz = bit-reversal of r % 16: 16 rows on 16 bank groups.
+//  kColOnly  swz = 4 (r % 4): the 4 rows of a transposed read in 4 quarters, lowest
+//            chunk bit untouched.
+//  kBoth     swz = 4 (r % 4) ^ 2 ((r / 8) % 2): transposed reads as kColOnly; row
+//            fragments 2-way at worst.
+// W = 64 packs two rows per 256-byte bank line and uses the analogous bits on r / 2;
+// W = 32 (only the dS^T tile, written by rows and read transposed) uses 2 ((r/8)%2).
+// Every transposed-readable variant satisfies swz(r + 4) == swz(r) for r % 8 < 4,
+// so a transposed fragment's second read (4 rows further down) reuses the first
+// read's lane offset, and every variant depends only on r % 16.
+enum TileMode { kBoth = 0, kRowOnly = 1, kColOnly = 2 };
+
+template <int W, int MODE>
 __device__ __forceinline__ int swz(int row) {
   if constexpr (W == 32) {
     return ((row >> 3) & 1) << 1;
   } else if constexpr (W == 64) {
-    return (((row >> 1) & 1) << 2) ^ (((row >> 3) & 1) << 1);
+    const int x = row >> 1;  // two rows share a bank line; x picks the 128-byte half's partner set
+    if constexpr (MODE == kRowOnly) return ((x & 1) << 2) | (x & 2) | ((x >> 2) & 1);
+    if constexpr (MODE == kColOnly) return (x & 1) << 2;
+    return ((x & 1) << 2) ^ (((row >> 3) & 1) << 1);
   } else {
+    if constexpr (MODE == kRowOnly) return ((row & 1) << 3) | (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    if constexpr (MODE == kColOnly) return (row & 3) << 2;
     return ((row & 3) << 2) ^ (((row >> 3) & 1) << 1);
   }
 }
 
-template <int W>
+template <int W, int MODE>
 __device__ __forceinline__ int tile_off(int row, int col) {  // byte offset of element (row, col)
-  return row * (2 * W) + ((((col >> 3) ^ swz<W>(row))) << 4) + ((col & 7) << 1);
+  return row * (2 * W) + ((((col >> 3) ^ swz<W, MODE>(row))) << 4) + ((col & 7) << 1);
 }
 
-// 8 consecutive elements of one row (col multiple of 8).
-template <int W>
-__device__ __forceinline__ bf16x8 row_frag(const LDS char* tile, int row, int col) {
-  return *(const LDS bf16x8*)(tile + tile_off<W>(row, col));
-}
-
-// Operand with the contraction index running down the tile's rows: lane l gets
-// tile[r0 + 8 * (l / 32) + e][c0 + l % 32], e = 0..7.  Each ds_read_b64_tr_b16
-// takes, per group of 16 lanes, four row segments of 4 elements and hands lane i
-// the four values of column i; lane j of the group supplies row j / 4, columns
-// 4 * (j % 4) .. +3.
-template <int W>
-__device__ __forceinline__ bf16x8 col_frag(const LDS char* tile, int r0, int c0, int lane) {
-  const int row = r0 + ((lane >> 5) << 3) + ((lane & 15) >> 2);
-  const int col = c0 + (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(tile + tile_off<W>(row, col)));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(tile + tile_off<W>(row + 4, col)));
-  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// Per-lane LDS byte offsets for the fragment reads of a W-wide swizzled tile.
-// Row fragments read rows R + pi(l % 32) (R a multiple of 32) at chunk 2 kk + l / 32;
-// transposed reads read rows r0 + 8 (l / 32) + (l % 16) / 4 (+4), r0 a multiple of
-// 16, at columns 32 db + 16 ((l / 16) % 2) + 4 (l % 4).  The swizzle only depends on
-// the row's low bits, so one register per chunk pattern covers every R / r0: the
-// row base and the chunk-pair above 16 (for W = 256) become compile-time constants
-// that fold into the ds_read immediate.  refresh() hides the values from loop-
-// invariant hoisting, which would otherwise materialise (and spill) one register
-// per (buffer, row, chunk) combination.
-template <int W>
-struct FragOffsets {
+// Per-lane LDS byte offsets for row fragments of a W-wide tile: rows R + pi(l % 32)
+// (R a multiple of 32) at elements 16 kk + 8 (l / 32) .. +7.  The swizzle only
+// depends on r % 16, so one register per chunk pattern covers every R: the row base
+// and the chunk-pair above 16 (W = 256) become compile-time constants folded into
+// the ds_read immediate.  refresh() hides the values from loop-invariant hoisting,
+// which would otherwise materialise (and spill) one register per (buffer, row,
+// chunk) combination.
+template <int W, int MODE>
+struct RowOffsets {
   static constexpr int NR = (W / 16) < 8 ? (W / 16) : 8;
-  static constexpr int NC = (W / 32) < 4 ? (W / 32) : 4;
   int rf[NR];
-  int cf[NC];
-  __device__ __forceinline__ void init(int lane) {
-    const int g = lane >> 5;
-    const int rrow = pi_row(lane & 31);
+  __device__ __forceinline__ void init(int lane, bool plain = false) {
+    const int rrow = plain ? (lane & 31) : pi_row(lane & 31);
 #pragma unroll
-    for (int kk = 0; kk < NR; ++kk) rf[kk] = tile_off<W>(rrow, kk * 16 + g * 8);
-    const int crow = ((lane >> 5) << 3) + ((lane & 15) >> 2);
-    const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
-#pragma unroll
-    for (int db = 0; db < NC; ++db) cf[db] = tile_off<W>(crow, db * 32 + ccol);
+    for (int kk = 0; kk < NR; ++kk) rf[kk] = tile_off<W, MODE>(rrow, kk * 16 + (lane >> 5) * 8);
   }
   __device__ __forceinline__ void refresh() {
 #pragma unroll
     for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(rf[i]));
+  }
+  __device__ __forceinline__ bf16x8 row(const LDS char* tile, int R, int kk) const {
+    return *(const LDS bf16x8*)(tile + R * (2 * W) + (kk / NR) * 256 + rf[kk % NR]);
+  }
+};
+
+// Per-lane offsets for transposed fragments: lane l gets
+// tile[r0 + 8 (l / 32) + e][32 db + l % 32], e = 0..7, r0 a multiple of 16.  Each
+// ds_read_b64_tr_b16 takes, per group of 16 lanes, four row segments of 4 elements
+// and hands lane i the four values of column i; lane j of the group supplies row
+// j / 4, columns 4 (j % 4) .. +3.
+template <int W, int MODE>
+struct ColOffsets {
+  static constexpr int NC = (W / 32) < 4 ? (W / 32) : 4;
+  int cf[NC];
+  __device__ __forceinline__ static int lane_off(int lane, int db) {
+    const int crow = ((lane >> 5) << 3) + ((lane & 15) >> 2);
+    const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
+    return tile_off<W, MODE>(crow, db * 32 + ccol);
+  }
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int db = 0; db < NC; ++db) cf[db] = lane_off(lane, db);
+  }
+  __device__ __forceinline__ void refresh() {
 #pragma unroll
     for (int i = 0; i < NC; ++i) asm volatile("" : "+v"(cf[i]));
   }
-  // Row fragment: rows R + pi(l % 32), elements 16 kk + 8 (l / 32) .. +7.
-  __device__ __forceinline__ bf16x8 row(const LDS char* tile, int R, int kk) const {
-    return *(const LDS bf16x8*)(tile + R * (2 * W) + (kk / NR) * 256 + rf[kk % NR]);
-  }
-  // Transposed fragment for a run-time db (computes the lane offset instead of
-  // indexing the register array, which would force it into scratch memory).
-  __device__ __forceinline__ static bf16x8 col_dyn(const LDS char* tile, int r0, int db, int lane) {
-    const int crow = ((lane >> 5) << 3) + ((lane & 15) >> 2);
-    const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
-    const LDS char* p = tile + r0 * (2 * W) + tile_off<W>(crow, db * 32 + ccol);
+  __device__ __forceinline__ static bf16x8 read_at(const LDS char* p) {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p);
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p + 4 * (2 * W)));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, v);
   }
-  // Transposed fragment: lane l gets tile[r0 + 8 (l / 32) + e][32 db + l % 32], e = 0..7.
   __device__ __forceinline__ bf16x8 col(const LDS char* tile, int r0, int db) const {
-    const LDS char* p = tile + r0 * (2 * W) + (db / NC) * 256 + cf[db % NC];
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)p);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS s16x4*)(p + 4 * (2 * W)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
+    return read_at(tile + r0 * (2 * W) + (db / NC) * 256 + cf[db % NC]);
   }
-};
-
-// Row fragments of rows R + l % 32 (plain order; the B operand of a product whose
-// contraction runs along the row, one row per lane column).
-template <int W>
-struct PlainRowOffsets {
-  static constexpr int NR = (W / 16) < 8 ? (W / 16) : 8;
-  int rf[NR];
-  __device__ __forceinline__ void init(int lane) {
-#pragma unroll
-    for (int kk = 0; kk < NR; ++kk) rf[kk] = tile_off<W>(lane & 31, kk * 16 + (lane >> 5) * 8);
-  }
-  __device__ __forceinline__ void refresh() {
-#pragma unroll
-    for (int i = 0; i < NR; ++i) asm volatile("" : "+v"(rf[i]));
-  }
-  __device__ __forceinline__ bf16x8 row(const LDS char* tile, int R, int kk) const {
-    return *(const LDS bf16x8*)(tile + R * (2 * W) + (kk / NR) * 256 + rf[kk % NR]);
-  }
-};
-
-// Register-staged copy of a ROWS x W bf16 tile from global memory (rows of pitch
-// W elements, rows >= valid_rows read as zeros) into the swizzled LDS layout.
-// NT threads cooperate; each moves ROWS * W / 8 / NT chunks of 16 bytes.
-template <int ROWS, int W, int NT>
-struct TileStager {
-  static constexpr int kChunks = ROWS * W / 8;
-  static constexpr int kPer = kChunks / NT;
-  static_assert(kChunks % NT == 0, "tile chunks must divide evenly over the threads");
-  u32x4 reg[kPer];
-
-  __device__ __forceinline__ void load(const __bf16* g, int row0, int valid_rows, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / (W / 8), c = idx % (W / 8);
-      if (row0 + r < valid_rows) {
-        reg[i] = *(const u32x4*)(g + (size_t)(row0 + r) * W + c * 8);
-      } else {
-        reg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(LDS char* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / (W / 8), c = idx % (W / 8);
-      *(LDS u32x4*)(tile + tile_off<W>(r, c * 8)) = reg[i];
-    }
+  // run-time db: computes the lane offset (indexing cf would force it into scratch)
+  __device__ __forceinline__ static bf16x8 col_dyn(const LDS char* tile, int r0, int db, int lane) {
+    return read_at(tile + r0 * (2 * W) + lane_off(lane, db));
   }
 };
 
@@ -216,7 +162,7 @@ struct TileStager {
 // valid_rows are clamped to the last valid row: the kernels mask such keys (-inf
 // scores) and give such queries P = 0, so the duplicated data never contributes.
 // The copy is asynchronous: wait_tile() (vmcnt) plus a barrier must precede reads.
-template <int ROWS, int W, int NW>
+template <int ROWS, int W, int NW, int MODE>
 struct TileDMA {
   static constexpr int kPieces = ROWS * W * 2 / 1024;
   static constexpr int kPerWave = kPieces / NW;
@@ -229,7 +175,7 @@ struct TileDMA {
       const int byte = piece * 1024 + lane * 16;
       const int row = byte / (2 * W);
       const int p = (byte % (2 * W)) >> 4;
-      const int c = p ^ swz<W>(row);
+      const int c = p ^ swz<W, MODE>(row);
       const int grow = min(row0 + row, valid_rows - 1);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + (size_t)grow * W + c * 8),
                                        (LDS void*)(tile + piece * 1024), 16, 0, 0);

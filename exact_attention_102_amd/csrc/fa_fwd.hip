@@ -40,13 +40,14 @@ struct FwdTileMath {
   // One K/V tile for one wave: 32 queries (one per lane column) x BC keys.
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               f32x16 (&o)[DB], float& m_run, float& l_run, float& lb_run, int k0,
-                                              int q_w, int qi, int N, float c, const FragOffsets<D>& fo, int g) {
+                                              int q_w, int qi, int N, float c, const RowOffsets<D, kRowOnly>& fk,
+                                              const ColOffsets<D, kColOnly>& fv, int g) {
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       s[kb] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(fo.row(kt, kb * 32, kk), qf[kk], s[kb]);
+      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(fk.row(kt, kb * 32, kk), qf[kk], s[kb]);
     }
     // keys past the end, and (causal) keys after the query, score -inf
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w)) {
@@ -101,7 +102,7 @@ struct FwdTileMath {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(fo.col(vt, ks * 16, db), pb[ks], o[db]);
+      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(fv.col(vt, ks * 16, db), pb[ks], o[db]);
     }
   }
 };
@@ -147,10 +148,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
-  using DMA = TileDMA<BC, D, NW>;
+  using KDMA = TileDMA<BC, D, NW, kRowOnly>;  // K: row fragments only
+  using VDMA = TileDMA<BC, D, NW, kColOnly>;  // V: transposed fragments only
 
-  DMA::issue(Kh, 0, N, kbuf0, wave, lane);
-  DMA::issue(Vh, 0, N, vbuf0, wave, lane);
+  KDMA::issue(Kh, 0, N, kbuf0, wave, lane);
+  VDMA::issue(Vh, 0, N, vbuf0, wave, lane);
 
   bf16x8 qf[KK];
   const int qrow = min(qi, N - 1);  // rows past the end duplicate the last row; never stored
@@ -161,29 +163,33 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = zero16();
-  FragOffsets<D> fo;
-  fo.init(lane);
+  RowOffsets<D, kRowOnly> fk;
+  fk.init(lane);
+  ColOffsets<D, kColOnly> fv;
+  fv.init(lane);
 
   wait_tile();
   __syncthreads();
   for (int j = 0; j < nkt; j += 2) {
-    fo.refresh();
+    fk.refresh();
+    fv.refresh();
     if (j + 1 < nkt) {
-      DMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
-      DMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
+      KDMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      VDMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     if (!CAUSAL || j * BC <= q_w + 31)
-      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fo, g);
+      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
-    fo.refresh();
+    fk.refresh();
+    fv.refresh();
     if (j + 2 < nkt) {
-      DMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
-      DMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
+      KDMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      VDMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (!CAUSAL || (j + 1) * BC <= q_w + 31)
-      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fo, g);
+      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g);
     wait_tile();
     __syncthreads();
   }
