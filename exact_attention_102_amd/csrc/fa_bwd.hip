@@ -257,7 +257,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   LDS char* vtile = (LDS char*)vts;
   LDS char* dst = (LDS char*)dsts;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nkt = (N + BK - 1) / BK;
@@ -284,13 +285,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const int key = kw + l32;
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
-  using QDMA = TileDMA<BQ, D, NW, kBoth>;  // Q, dO: row fragments and transposed reads
   constexpr int KMODE = M::KMODE;
-
-  QDMA::issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
-  QDMA::issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
-  if constexpr (ATOMIC || KV_LDS) TileDMA<BK, D, NW, KMODE>::issue(Kh, k0, N, ktile, wave, lane);
-  if constexpr (KV_LDS) TileDMA<BK, D, NW, kRowOnly>::issue(Vh, k0, N, vtile, wave, lane);
+  TileDMA<BQ, D, NW, kBoth> qdma;  // Q, dO: row fragments and transposed reads
+  qdma.init(wave, lane);
+  qdma.issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
+  qdma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
+  if constexpr (ATOMIC || KV_LDS) {
+    TileDMA<BK, D, NW, KMODE> kd;
+    kd.init(wave, lane);
+    kd.issue(Kh, k0, N, ktile, wave, lane);
+  }
+  if constexpr (KV_LDS) {
+    TileDMA<BK, D, NW, kRowOnly> vd;
+    vd.init(wave, lane);
+    vd.issue(Vh, k0, N, vtile, wave, lane);
+  }
   RowStager<BQ, NT> srow;
   srow.load(lseh, delh, qt0 * BQ, N, tid);
   srow.store(st0, tid);
@@ -330,9 +339,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pk.refresh();
       pv.refresh();
     }
+    qdma.refresh();
     if (it + 1 < nqt) {
-      QDMA::issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
-      QDMA::issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
+      qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
+      qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
       srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
     M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
@@ -347,9 +357,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pk.refresh();
       pv.refresh();
     }
+    qdma.refresh();
     if (it + 2 < nqt) {
-      QDMA::issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
-      QDMA::issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
+      qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
+      qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
       srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, dst, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N, c, a.scale,
@@ -443,7 +454,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   LDS char* kbuf1 = (LDS char*)k1s;
   LDS char* vbuf1 = (LDS char*)v1s;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BR - 1) / BR;
@@ -468,11 +480,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
-  using KDMA = TileDMA<BC, D, NW, kBoth>;     // K: row fragments and transposed reads
-  using VDMA = TileDMA<BC, D, NW, kRowOnly>;  // V: row fragments only
-
-  KDMA::issue(Kh, 0, N, kbuf0, wave, lane);
-  VDMA::issue(Vh, 0, N, vbuf0, wave, lane);
+  TileDMA<BC, D, NW, kBoth> kdma;     // K: row fragments and transposed reads
+  TileDMA<BC, D, NW, kRowOnly> vdma;  // V: row fragments only
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
+  kdma.issue(Kh, 0, N, kbuf0, wave, lane);
+  vdma.issue(Vh, 0, N, vbuf0, wave, lane);
 
   const int qrow = min(qi, N - 1);  // rows past the end get lse = +inf (P = 0) and are never stored
   bf16x8 qf[KK], dof[KK];
@@ -499,9 +512,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     fkr.refresh();
     fkc.refresh();
     fvr.refresh();
+    kdma.refresh();
+    vdma.refresh();
     if (j + 1 < nkt) {
-      KDMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
-      VDMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
+      kdma.issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      vdma.issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     // waves wholly past the end (padding rows) or below this key tile's diagonal skip the tile
     if (q_w < N && (!CAUSAL || j * BC <= q_w + 31))
@@ -512,9 +527,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     fkr.refresh();
     fkc.refresh();
     fvr.refresh();
+    kdma.refresh();
+    vdma.refresh();
     if (j + 2 < nkt) {
-      KDMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
-      VDMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
+      kdma.issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (q_w < N && (!CAUSAL || (j + 1) * BC <= q_w + 31))
       M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fkr, fkc, fvr, g);

@@ -158,27 +158,60 @@ struct ColOffsets {
 // Direct-to-LDS copy of a ROWS x W bf16 tile (global_load_lds_dwordx4): each wave
 // instruction moves 64 x 16 bytes straight into 1 KB of contiguous LDS (lane l
 // lands at base + 16 l), bypassing registers.  Lane l therefore fetches the global
-// chunk that belongs at its LDS position under the swizzle.  Rows at or beyond
-// valid_rows are clamped to the last valid row: the kernels mask such keys (-inf
-// scores) and give such queries P = 0, so the duplicated data never contributes.
+// chunk that belongs at its LDS position under the swizzle.  The per-lane byte
+// offsets of the pieces are computed once (init) and kept opaque to the optimiser
+// (refresh); each issue is then one VALU-free instruction with a wave-uniform
+// (SGPR) row base and the LDS destination in M0.  Tiles reaching past valid_rows
+// take a slower path that clamps rows to the last valid one: the kernels mask such
+// keys (-inf scores) and give such queries P = 0, so the duplicates never count.
 // The copy is asynchronous: wait_tile() (vmcnt) plus a barrier must precede reads.
 template <int ROWS, int W, int NW, int MODE>
 struct TileDMA {
   static constexpr int kPieces = ROWS * W * 2 / 1024;
   static constexpr int kPerWave = kPieces / NW;
   static_assert(kPieces % NW == 0, "tile must split into whole 1 KB pieces per wave");
-  __device__ __forceinline__ static void issue(const __bf16* g, int row0, int valid_rows, LDS char* tile, int wave,
-                                               int lane) {
+  unsigned off[kPerWave];
+
+  __device__ __forceinline__ static int piece_row(int piece, int lane) { return (piece * 1024 + lane * 16) / (2 * W); }
+  __device__ __forceinline__ static int piece_chunk(int piece, int lane) {
+    const int byte = piece * 1024 + lane * 16;
+    return ((byte % (2 * W)) >> 4) ^ swz<W, MODE>(byte / (2 * W));
+  }
+  __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int piece = i * NW + wave;
-      const int byte = piece * 1024 + lane * 16;
-      const int row = byte / (2 * W);
-      const int p = (byte % (2 * W)) >> 4;
-      const int c = p ^ swz<W, MODE>(row);
-      const int grow = min(row0 + row, valid_rows - 1);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(g + (size_t)grow * W + c * 8),
-                                       (LDS void*)(tile + piece * 1024), 16, 0, 0);
+      off[i] = (unsigned)(piece_row(piece, lane) * (2 * W) + piece_chunk(piece, lane) * 16);
+    }
+  }
+  __device__ __forceinline__ void refresh() {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) asm volatile("" : "+v"(off[i]));
+  }
+  // wave must be wave-uniform (e.g. readfirstlane of threadIdx.x / 64).
+  __device__ __forceinline__ void issue(const __bf16* g, int row0, int valid_rows, LDS char* tile, int wave,
+                                        int lane) const {
+    if (row0 + ROWS <= valid_rows) {
+      // one uniform 64-bit base (SGPR pair) so each issue is base + 32-bit lane offset
+      const unsigned long long b = (unsigned long long)(g + (size_t)row0 * W);
+      const unsigned blo = __builtin_amdgcn_readfirstlane((unsigned)b);
+      const unsigned bhi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+      const __attribute__((address_space(1))) char* base =
+          (const __attribute__((address_space(1))) char*)(((unsigned long long)bhi << 32) | blo);
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off[i]),
+                                         (LDS void*)(tile + (i * NW + wave) * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int piece = i * NW + wave;
+        const int grow = min(row0 + piece_row(piece, lane), valid_rows - 1);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(g + (size_t)grow * W + piece_chunk(piece, lane) * 8),
+            (LDS void*)(tile + piece * 1024), 16, 0, 0);
+      }
     }
   }
 };

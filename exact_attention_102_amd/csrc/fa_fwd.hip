@@ -124,7 +124,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   LDS char* kbuf1 = (LDS char*)k1s;
   LDS char* vbuf1 = (LDS char*)v1s;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BR - 1) / BR;
@@ -148,11 +149,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const int q_last = min(N, q_wg + BR) - 1;
   const int kv_end = CAUSAL ? q_last + 1 : N;
   const int nkt = (kv_end + BC - 1) / BC;
-  using KDMA = TileDMA<BC, D, NW, kRowOnly>;  // K: row fragments only
-  using VDMA = TileDMA<BC, D, NW, kColOnly>;  // V: transposed fragments only
-
-  KDMA::issue(Kh, 0, N, kbuf0, wave, lane);
-  VDMA::issue(Vh, 0, N, vbuf0, wave, lane);
+  TileDMA<BC, D, NW, kRowOnly> kdma;  // K: row fragments only
+  TileDMA<BC, D, NW, kColOnly> vdma;  // V: transposed fragments only
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
+  kdma.issue(Kh, 0, N, kbuf0, wave, lane);
+  vdma.issue(Vh, 0, N, vbuf0, wave, lane);
 
   bf16x8 qf[KK];
   const int qrow = min(qi, N - 1);  // rows past the end duplicate the last row; never stored
@@ -173,9 +175,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   for (int j = 0; j < nkt; j += 2) {
     fk.refresh();
     fv.refresh();
+    kdma.refresh();
+    vdma.refresh();
     if (j + 1 < nkt) {
-      KDMA::issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
-      VDMA::issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
+      kdma.issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
+      vdma.issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     if (!CAUSAL || j * BC <= q_w + 31)
       M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g);
@@ -184,9 +188,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     if (j + 1 >= nkt) break;
     fk.refresh();
     fv.refresh();
+    kdma.refresh();
+    vdma.refresh();
     if (j + 2 < nkt) {
-      KDMA::issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
-      VDMA::issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
+      kdma.issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
+      vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (!CAUSAL || (j + 1) * BC <= q_w + 31)
       M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g);
