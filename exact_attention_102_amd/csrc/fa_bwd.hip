@@ -72,19 +72,24 @@ int launch_preprocess(const PreArgs& a, int d, hipStream_t stream) {
 // that P = 0 there) and delta (0 past the end).
 template <int BQ, int NT>
 struct RowStager {
-  float v;
+  float raw;
+  int q;
+  // Issues the load only; nothing reads it until store(), which runs after the
+  // tile's wait (wait_tile), so the load never makes the wave wait for the
+  // direct-to-LDS prefetch issued after it.
   __device__ __forceinline__ void load(const float* lse, const float* delta, int q0, int N, int tid) {
-    v = 0.f;
-    if (tid < BQ) {
-      const int q = q0 + tid;
-      v = q < N ? lse[q] * kLog2e : INFINITY;
-    } else if (tid < 2 * BQ) {
-      const int q = q0 + tid - BQ;
-      v = q < N ? delta[q] : 0.f;
-    }
+    const int r = tid < BQ ? tid : tid - BQ;
+    q = q0 + r;
+    const float* src = tid < BQ ? lse : delta;
+    raw = tid < 2 * BQ ? src[min(q, N - 1)] : 0.f;
   }
-  __device__ __forceinline__ void store(LDS float* dst, int tid) const {
-    if (tid < 2 * BQ) dst[tid] = v;
+  __device__ __forceinline__ void store(LDS float* dst, int N, int tid) {
+    asm volatile("" : "+v"(raw));  // keeps every use of the loaded value after this point
+    if (tid < BQ) {
+      dst[tid] = q < N ? raw * kLog2e : INFINITY;
+    } else if (tid < 2 * BQ) {
+      dst[tid] = q < N ? raw : 0.f;
+    }
   }
 };
 
@@ -111,6 +116,9 @@ struct DkdvMath {
   static constexpr int QBN = BQ / 32;
   static constexpr int DB = D / 32;
   static constexpr int KK = D / 16;
+  // LDS fragment reads issued ahead of their MFMAs (needs registers the d = 256 and
+  // the 8-wave atomic shapes do not have; those keep short scheduling fences)
+  static constexpr bool kReadAhead = D <= 128 && !(ATOMIC && NW > 4);
 
   __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
@@ -144,7 +152,19 @@ struct DkdvMath {
           }
           s = mfma32(fr.row(qtl, qb * 32, kk), kb, s);
           dp = mfma32(fr.row(dotl, qb * 32, kk), vb, dp);
-          fence_every<4>(kk);
+          if constexpr (!kReadAhead) fence_every<4>(kk);
+        }
+        // Interleave: fragment reads run two k-steps ahead of their MFMAs, so LDS
+        // latency hides under the previous products instead of stalling the wave.
+        if constexpr (kReadAhead) {
+          constexpr int RPS = KV_LDS ? 4 : 2;  // row-fragment reads per k-step
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
+#pragma unroll
+          for (int kk = 0; kk < KK - 2; ++kk) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
         // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
@@ -188,7 +208,17 @@ struct DkdvMath {
           dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
           dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
           dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
-          fence_every<2>(db);
+          if constexpr (!kReadAhead) fence_every<2>(db);
+        }
+        // transposed reads (8 per d block) run one d block ahead of their 4 MFMAs
+        if constexpr (kReadAhead) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int db = 0; db < DB - 1; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         if constexpr (ATOMIC) {
           if (!CAUSAL && key >= N) {
@@ -302,7 +332,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   }
   RowStager<BQ, NT> srow;
   srow.load(lseh, delh, qt0 * BQ, N, tid);
-  srow.store(st0, tid);
+  srow.store(st0, N, tid);
 
   bf16x8 kf[KV_LDS ? 1 : KK], vf[KV_LDS ? 1 : KK];
   if constexpr (!KV_LDS) {
@@ -347,8 +377,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     }
     M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
             pk, pv, wave, g, l32, lane);
-    if (it + 1 < nqt) srow.store(st1, tid);
     wait_tile();
+    if (it + 1 < nqt) srow.store(st1, N, tid);
     __syncthreads();
     if (it + 1 >= nqt) break;
     fr.refresh();
@@ -365,8 +395,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     }
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, dst, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N, c, a.scale,
             fr, fc, pk, pv, wave, g, l32, lane);
-    if (it + 2 < nqt) srow.store(st0, tid);
     wait_tile();
+    if (it + 2 < nqt) srow.store(st0, N, tid);
     __syncthreads();
   }
 

@@ -23,6 +23,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt 7, lgkmcnt 15 (only vmcnt waits)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 namespace fa {
 
@@ -155,16 +157,59 @@ struct ColOffsets {
   }
 };
 
-// Direct-to-LDS copy of a ROWS x W bf16 tile (global_load_lds_dwordx4): each wave
-// instruction moves 64 x 16 bytes straight into 1 KB of contiguous LDS (lane l
-// lands at base + 16 l), bypassing registers.  Lane l therefore fetches the global
-// chunk that belongs at its LDS position under the swizzle.  The per-lane byte
-// offsets of the pieces are computed once (init) and kept opaque to the optimiser
-// (refresh); each issue is then one VALU-free instruction with a wave-uniform
-// (SGPR) row base and the LDS destination in M0.  Tiles reaching past valid_rows
-// take a slower path that clamps rows to the last valid one: the kernels mask such
-// keys (-inf scores) and give such queries P = 0, so the duplicates never count.
-// The copy is asynchronous: wait_tile() (vmcnt) plus a barrier must precede reads.
+// One direct-to-LDS copy instruction (buffer_load_dwordx4 ... lds): lane l reads 16
+// bytes at rsrc.base + soff + voff and writes them to LDS at lds + 16 l (M0 holds
+// the LDS base; s_nop covers the M0-write -> LDS-DMA hazard).
+//
+// It is issued from inline assembly on purpose.  Through the compiler builtins,
+// either form (global_load_lds, buffer_load ... lds) damages the wait-count
+// placement of every LDS fragment read in the kernel: the global form is
+// FLAT-class, so LDS-side completions are modelled as out of order and each read
+// waits for all outstanding ones (lgkmcnt(0)); the buffer form is tracked as an
+// asynchronous LDS store that every later LDS read is assumed to alias, so each
+// read also waits for the in-flight prefetch of the next tile (vmcnt).  Here the
+// compiler does not see the copy; the kernels order it themselves: wait_tile()
+// (vmcnt(0)) and a barrier before a tile is read, and a barrier (which drains
+// outstanding LDS reads) before a buffer is refilled.  Compiler-placed vmcnt waits
+// for its own loads only over-wait when these copies are outstanding (the counter
+// retires in order), so they stay correct.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt 7, lgkmcnt 15 (only vmcnt waits)
+constexpr int kWaitVmcnt0 = 0x0F70;
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, unsigned voff, unsigned soff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(soff), "s"(lds)
+               : "m0");
+}
+
+// Buffer resource for raw dword loads over [base, base + bytes): word 1 holds
+// address bits 32..47 with stride 0; word 3 selects data format 32 (the field must
+// be non-zero for untyped loads), no swizzle, no index.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((unsigned)b);
+  r[1] = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32) & 0xffffu);
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000u;
+  return r;
+}
+
+__device__ __forceinline__ unsigned lds_addr(const LDS void* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)p);
+}
+
+// Direct-to-LDS copy of a ROWS x W bf16 tile: each wave instruction moves 64 x 16
+// bytes straight into 1 KB of contiguous LDS (lane l lands at base + 16 l),
+// bypassing registers.  Lane l therefore fetches the global chunk that belongs at
+// its LDS position under the swizzle.  The per-lane byte offsets of the pieces are
+// computed once (init) and kept opaque to the optimiser (refresh); each issue is
+// then one VALU-free instruction with a wave-uniform (SGPR) row offset.  Tiles
+// reaching past valid_rows take a slower path that clamps rows to the last valid
+// one: the kernels mask such keys (-inf scores) and give such queries P = 0, so the
+// duplicates never count.  The copy is asynchronous: wait_tile() (vmcnt) plus a
+// barrier must precede reads.
 template <int ROWS, int W, int NW, int MODE>
 struct TileDMA {
   static constexpr int kPieces = ROWS * W * 2 / 1024;
@@ -188,35 +233,31 @@ struct TileDMA {
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) asm volatile("" : "+v"(off[i]));
   }
-  // wave must be wave-uniform (e.g. readfirstlane of threadIdx.x / 64).
+  // wave must be wave-uniform (e.g. readfirstlane of threadIdx.x / 64); g is the
+  // head's base and valid_rows its row count (valid_rows * 2W < 2^32 bytes, so
+  // every offset fits the 32-bit buffer range, which also bounds the reads).
   __device__ __forceinline__ void issue(const __bf16* g, int row0, int valid_rows, LDS char* tile, int wave,
                                         int lane) const {
+    const u32x4 rs = buffer_rsrc(g, (unsigned)valid_rows * (2u * W));
     if (row0 + ROWS <= valid_rows) {
-      // one uniform 64-bit base (SGPR pair) so each issue is base + 32-bit lane offset
-      const unsigned long long b = (unsigned long long)(g + (size_t)row0 * W);
-      const unsigned blo = __builtin_amdgcn_readfirstlane((unsigned)b);
-      const unsigned bhi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
-      const __attribute__((address_space(1))) char* base =
-          (const __attribute__((address_space(1))) char*)(((unsigned long long)bhi << 32) | blo);
+      const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)row0 * (2u * W));
 #pragma unroll
-      for (int i = 0; i < kPerWave; ++i) {
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off[i]),
-                                         (LDS void*)(tile + (i * NW + wave) * 1024), 16, 0, 0);
-      }
+      for (int i = 0; i < kPerWave; ++i) lds_dma16(rs, off[i], soff, lds_addr(tile + (i * NW + wave) * 1024));
     } else {
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
         const int piece = i * NW + wave;
         const int grow = min(row0 + piece_row(piece, lane), valid_rows - 1);
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)(g + (size_t)grow * W + piece_chunk(piece, lane) * 8),
-            (LDS void*)(tile + piece * 1024), 16, 0, 0);
+        lds_dma16(rs, (unsigned)grow * (2u * W) + (unsigned)piece_chunk(piece, lane) * 16u, 0u,
+                  lds_addr(tile + piece * 1024));
       }
     }
   }
 };
 
-__device__ __forceinline__ void wait_tile() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0) through the builtin (not inline assembly), so the compiler's own
+// wait-count tracking also learns that all of its vector-memory loads are done.
+__device__ __forceinline__ void wait_tile() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); }
 
 // Scheduling fence every CH iterations of an unrolled loop: bounds how many LDS
 // fragment reads the scheduler hoists ahead of their MFMAs (each costs 4 VGPRs).
