@@ -36,6 +36,8 @@ struct FwdTileMath {
   static constexpr int KB = BC / 32;  // 32-key blocks per tile
   static constexpr int DB = D / 32;   // 32-wide blocks of the head dim
   static constexpr int KK = D / 16;   // k-steps of Q K^T
+  static constexpr int kAhead = 3;
+  static constexpr int kAheadV = 3;
 
   // One K/V tile for one wave: 32 queries (one per lane column) x BC keys.
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
@@ -44,11 +46,21 @@ struct FwdTileMath {
                                               const ColOffsets<D, kColOnly>& fv, int g) {
     f32x16 s[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = zero16();
+    for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) s[kb] = mfma32(fk.row(kt, kb * 32, kk), qf[kk], s[kb]);
+    for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(fk.row(kt, kb * 32, kk), qf[kk], s[kb]);
     }
+    // K fragment reads run kAhead k-steps ahead of their MFMAs (LDS latency hides
+    // under the previous k-steps' products)
+    __builtin_amdgcn_sched_group_barrier(0x100, KB * kAhead, 0);
+#pragma unroll
+    for (int kk = 0; kk < KK - kAhead; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, KB * kAhead, 0);
     // keys past the end, and (causal) keys after the query, score -inf
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w)) {
 #pragma unroll
@@ -100,10 +112,18 @@ struct FwdTileMath {
     l_run += rs;
     lb_run += rb;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int ks = 0; ks < 2 * KB; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 2 * KB; ++ks) o[db] = mfma32(fv.col(vt, ks * 16, db), pb[ks], o[db]);
+      for (int db = 0; db < DB; ++db) o[db] = mfma32(fv.col(vt, ks * 16, db), pb[ks], o[db]);
     }
+    // transposed V reads (two per MFMA) run kAheadV MFMAs ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAheadV, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KB * DB - kAheadV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kAheadV, 0);
   }
 };
 
