@@ -23,8 +23,6 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt 7, lgkmcnt 15 (only vmcnt waits)
-constexpr int kWaitVmcnt0 = 0x0F70;
 
 namespace fa {
 
@@ -159,7 +157,11 @@ struct ColOffsets {
 
 // One direct-to-LDS copy instruction (buffer_load_dwordx4 ... lds): lane l reads 16
 // bytes at rsrc.base + soff + voff and writes them to LDS at lds + 16 l (M0 holds
-// the LDS base; s_nop covers the M0-write -> LDS-DMA hazard).
+// the LDS base; s_nop covers the M0-write -> LDS-DMA hazard).  M0 is written inside
+// the statement and declared clobbered; nothing else in these kernels uses M0 (no
+// LDS-DMA builtins, GWS or indexed register moves).  Passing the base as an "{m0}"
+// operand instead leaves the compiler short of SGPRs (every tile's LDS base stays
+// live in one), and that build faulted the GPU, so it is not used.
 //
 // It is issued from inline assembly on purpose.  Through the compiler builtins,
 // either form (global_load_lds, buffer_load ... lds) damages the wait-count
@@ -173,9 +175,10 @@ struct ColOffsets {
 // outstanding LDS reads) before a buffer is refilled.  Compiler-placed vmcnt waits
 // for its own loads only over-wait when these copies are outstanding (the counter
 // retires in order), so they stay correct.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt 7, lgkmcnt 15 (only vmcnt waits)
 constexpr int kWaitVmcnt0 = 0x0F70;
+// s_waitcnt immediate for vmcnt(n), n < 64 (vmcnt bits 3:0 and 15:14)
+constexpr int vmcnt_wait(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
 __device__ __forceinline__ void lds_dma16(const u32x4& rsrc, unsigned voff, unsigned soff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
