@@ -81,7 +81,7 @@ int default_index(int pass, int d, int causal) {
     case 0: return d == 64 ? 2 : 0;                   // fwd: d64 Br32x8 Bc64, d128 Br32x4 Bc64, d256 Bc32
     case 1: return d == 64 ? 2 : (d == 128 && causal) ? 3 : 0;  // dkdv: d64 Bk32x8 Bq64, d128 Bk32x4 Bq64
                                                                  // (causal: K/V in LDS)
-    case 2: return d == 64 ? 2 : 0;                   // dkdv + atomic dq
+    case 2: return d == 64 ? 3 : 0;                   // dkdv + atomic dq: d64 Bk32x8 Bq64 deferred
     case 3: return (d == 128 && !causal) ? 2 : 0;     // dq: d128 non-causal Bq32x8 Bc64
     default: return -1;
   }

@@ -239,8 +239,16 @@ struct DkdvMath {
         *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = z;
       }
     }
-    if constexpr (ATOMIC) {
-      __syncthreads();
+  }
+
+  // 5-GEMM: dQ_tile = dS K over the workgroup's BK keys (its dS^T blocks in LDS,
+  // written by tile() of the previous query tile and made visible by the barrier
+  // that ended it), one fp32 atomic per dq element per workgroup.  Running it one
+  // tile late lets the atomics drain under the next tile's products instead of
+  // holding up the end-of-tile wait.
+  __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
+                                                   int N, float scale, int wave, int g, int l32, int lane) {
+    {
       for (int t = wave; t < QBN * DB; t += NW) {
         const int qb = t / DB, db = t % DB;
         f32x16 acc = zero16();
@@ -259,7 +267,9 @@ struct DkdvMath {
   }
 };
 
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS>
+// DEFER (atomic only): the dQ product and atomics of a query tile run at the start
+// of the next tile, from a second dS^T buffer, instead of behind an extra barrier.
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   using M = DkdvMath<D, BQ, NW, CAUSAL, ATOMIC, KV_LDS>;
   constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
@@ -277,6 +287,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kts[KT_BYTES];
   __shared__ __attribute__((aligned(1024))) char vts[VT_BYTES];
   __shared__ __attribute__((aligned(1024))) char dsts[DST_BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsts1[DEFER ? DST_BYTES : 16];  // dS^T of alternate query tiles
   LDS char* qbuf0 = (LDS char*)q0s;
   LDS char* dbuf0 = (LDS char*)d0s;
   LDS char* qbuf1 = (LDS char*)q1s;
@@ -285,7 +296,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   LDS float* st1 = (LDS float*)st1s;
   LDS char* ktile = (LDS char*)kts;
   LDS char* vtile = (LDS char*)vts;
-  LDS char* dst = (LDS char*)dsts;
+  LDS char* dst0 = (LDS char*)dsts;
+  LDS char* dst1 = (LDS char*)dsts1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -375,8 +387,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
       srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
-    M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
+    if constexpr (ATOMIC && DEFER) {
+      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
+    }
+    M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst0, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
             pk, pv, wave, g, l32, lane);
+    if constexpr (ATOMIC && !DEFER) {
+      __syncthreads();
+      M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
+    }
     wait_tile();
     if (it + 1 < nqt) srow.store(st1, N, tid);
     __syncthreads();
@@ -393,11 +412,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
       srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
-    M::tile(qbuf1, dbuf1, st1, ktile, vtile, dst, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N, c, a.scale,
-            fr, fc, pk, pv, wave, g, l32, lane);
+    if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
+    M::tile(qbuf1, dbuf1, st1, ktile, vtile, DEFER ? dst1 : dst0, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N,
+            c, a.scale, fr, fc, pk, pv, wave, g, l32, lane);
+    if constexpr (ATOMIC && !DEFER) {
+      __syncthreads();
+      M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane);
+    }
     wait_tile();
     if (it + 2 < nqt) srow.store(st0, N, tid);
     __syncthreads();
+  }
+  if constexpr (ATOMIC && DEFER) {  // dQ of the last query tile (its dS^T buffer alternates with the tile's parity)
+    const int last = nqt - 1;
+    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane);
   }
 
   if (key < N) {
@@ -584,18 +612,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int BQ, int NW, bool ATOMIC, bool KV_LDS>
+template <int D, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false>
 static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 32 * NW;
   const int nkt = (a.N + BK - 1) / BK;
   const long long blocks = (long long)a.B * a.H * nkt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, true, ATOMIC, KV_LDS>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, true, ATOMIC, KV_LDS, DEFER>), dim3((unsigned)blocks), dim3(NW * 64),
+                       0, stream, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, false, ATOMIC, KV_LDS>), dim3((unsigned)blocks), dim3(NW * 64), 0,
-                       stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, false, ATOMIC, KV_LDS, DEFER>), dim3((unsigned)blocks), dim3(NW * 64),
+                       0, stream, a);
   }
   return 0;
 }
@@ -618,6 +646,11 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, false, KVL> }
 #define DKDVA_CFG(D, BQ, NW, KVL) \
   { D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, true, KVL> }
+#define DKDVAD_CFG(D, BQ, NW, KVL)                                                                       \
+  {                                                                                                        \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " deferred",         \
+        &launch_dkdv<D, BQ, NW, true, KVL, true>                                                           \
+  }
 #define DQ_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC> }
 
@@ -635,7 +668,8 @@ const BwdConfig* dkdv_configs(int* count) {
 const BwdConfig* dkdv_atomic_configs(int* count) {
   static const BwdConfig table[] = {
       DKDVA_CFG(64, 64, 4, false),  DKDVA_CFG(64, 32, 4, false),  DKDVA_CFG(64, 64, 8, false),
-      DKDVA_CFG(128, 64, 4, false), DKDVA_CFG(128, 32, 4, false),
+      DKDVAD_CFG(64, 64, 8, false),
+      DKDVA_CFG(128, 64, 4, false), DKDVA_CFG(128, 32, 4, false), DKDVAD_CFG(128, 64, 4, false),
       DKDVA_CFG(256, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
