@@ -158,3 +158,28 @@ def test_d_spectrum_matches_the_page():
     g = json.load(open(os.path.join(GOLDEN, "d_spectrum.json")))
     assert d_spectrum() == g["values"]
     assert len(g["values"]) == 42
+
+
+def test_report_tile_counts_match_brute_force():
+    """Tile accounting of the per-configuration report: loaded tiles per head for the query-major passes
+    (forward, dQ) and the key-major dK/dV pass, against an explicit walk over the tile grid."""
+    import itertools
+
+    from exact_attention_102_amd.report import tile_shape, tiles
+
+    assert tile_shape("fwd d128 Br32x4 Bc64 occ2") == (128, 64)
+    assert tile_shape("dkdv+atomic-dq d64 Bk32x8 Bq64 kv_ldsfalse deferred") == (256, 64)
+
+    def walk(N, rows, cols, causal, keys_major):
+        nr, nc = -(-N // rows), -(-N // cols)
+        seen = 0
+        for r, c in itertools.product(range(nr), range(nc)):
+            if keys_major:  # key block r meets query tile c unless every query precedes every key
+                seen += (not causal) or min(N, (c + 1) * cols) - 1 >= r * rows
+            else:  # query block r meets key tile c unless every key follows every query
+                seen += (not causal) or c * cols <= min(N, (r + 1) * rows) - 1
+        return seen, nr * nc
+
+    for N, rows, cols, causal, km in itertools.product([1, 33, 300, 2048], [64, 128, 256], [32, 64], [False, True],
+                                                      [False, True]):
+        assert tiles(N, rows, cols, causal, km) == walk(N, rows, cols, causal, km)
