@@ -24,6 +24,11 @@ PASS_FWD, PASS_DKDV, PASS_DKDV_ATOMIC, PASS_DQ = 0, 1, 2, 3
 _lib = None
 
 
+class FaStrides(ctypes.Structure):
+    """fa_strides: element strides (b, h, n) of a [B, H, N, d] view with a contiguous head dim."""
+    _fields_ = [("b", ctypes.c_longlong), ("h", ctypes.c_longlong), ("n", ctypes.c_longlong)]
+
+
 class FAError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__("%s: %s" % (what, fa_status_string(status)))
@@ -66,6 +71,16 @@ def lib() -> ctypes.CDLL:
     L.fa_status_string.restype = cp
     L.fa_version.argtypes = []
     L.fa_version.restype = cp
+    st = FaStrides
+    L.fa_fwd_general_workspace_size.argtypes = [i, i, i, i]
+    L.fa_fwd_general_workspace_size.restype = sz
+    L.fa_bwd_general_workspace_size.argtypes = [i, i, i, i, i]
+    L.fa_bwd_general_workspace_size.restype = sz
+    L.fa_fwd_general.argtypes = [vp, st, vp, st, vp, st, i, i, i, i, i, f, vp, st, vp, vp, sz, vp]
+    L.fa_fwd_general.restype = i
+    L.fa_bwd_general.argtypes = [vp, st, vp, st, vp, st, vp, st, vp, vp, st, i, i, i, i, i, f, i,
+                                 vp, st, vp, st, vp, st, vp, sz, vp]
+    L.fa_bwd_general.restype = i
     _lib = L
     return L
 
@@ -220,3 +235,79 @@ def fa_bwd_dq(q, k, v, dout, lse, delta, causal: bool, scale: float, dq, stream=
     if st != FA_OK:
         raise FAError(st, "fa_bwd_dq")
     return dq
+
+
+# --------------------------------------------------------------------------- general entry points
+def _view(t, name, dtype, shape):
+    """Pointer and strides of a [B, H, N, d] view whose last dimension is contiguous."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError("%s: the head dimension must be contiguous (stride 1)" % name)
+    return ctypes.c_void_p(t.data_ptr()), FaStrides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def fa_fwd_general_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(lib().fa_fwd_general_workspace_size(int(B), int(H), int(N), int(d)))
+
+
+def fa_bwd_general_workspace_size(B: int, H: int, N: int, d: int, variant: int = FA_BWD_7GEMM) -> int:
+    return int(lib().fa_bwd_general_workspace_size(int(B), int(H), int(N), int(d), int(variant)))
+
+
+def _workspace(need, device, workspace):
+    torch = _torch()
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, workspace=None, stream=None):
+    """Forward for any head dim 1..256 and strided [B, H, N, d] views (e.g. a [B, N, H, d] tensor
+    transposed); returns (o, lse).  o defaults to a new contiguous fp32 tensor."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    pq, sq = _view(q, "q", torch.bfloat16, q.shape)
+    pk, sk = _view(k, "k", torch.bfloat16, q.shape)
+    pv, sv = _view(v, "v", torch.bfloat16, q.shape)
+    if o is None:
+        o = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    po, so = _view(o, "o", torch.float32, q.shape)
+    pl = _check(lse, "lse", torch.float32, (B, H, N))
+    workspace, pw, wb = _workspace(fa_fwd_general_workspace_size(B, H, N, d), q.device, workspace)
+    st = lib().fa_fwd_general(pq, sq, pk, sk, pv, sv, B, H, N, d, int(bool(causal)), float(scale), po, so, pl, pw, wb,
+                              _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_general")
+    return o, lse
+
+
+def fa_bwd_general(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
+                   dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward for any head dim 1..256 and strided views; returns (dq, dk, dv) (new contiguous fp32
+    tensors unless given)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    args = [_view(q, "q", torch.bfloat16, q.shape), _view(k, "k", torch.bfloat16, q.shape),
+            _view(v, "v", torch.bfloat16, q.shape), _view(o, "o", torch.float32, q.shape)]
+    pl = _check(lse, "lse", torch.float32, (B, H, N))
+    pdo, sdo = _view(dout, "dout", torch.bfloat16, q.shape)
+    outs = [t if t is not None else torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+            for t in (dq, dk, dv)]
+    pouts = [_view(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
+    workspace, pw, wb = _workspace(fa_bwd_general_workspace_size(B, H, N, d, variant), q.device, workspace)
+    flat = [x for pair in args for x in pair]
+    st = lib().fa_bwd_general(*flat, pl, pdo, sdo, B, H, N, d, int(bool(causal)), float(scale), int(variant),
+                              *[x for pair in pouts for x in pair], pw, wb, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_general")
+    return tuple(outs)

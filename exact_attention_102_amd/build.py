@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_pad.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 # Packed-fp32 instructions are disabled: the compiler must not emit v_pk_{add,mul,fma}_f32.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -362,3 +362,192 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// General entry points (any d in 1..256, strided views): padded contiguous copies.
+namespace {
+
+constexpr int kMaxGeneralD = 256;
+
+int padded_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa::View view_of(fa_strides s) { return fa::View{s.b, s.h, s.n}; }
+
+bool contiguous(fa_strides s, int H, int N, int d) {
+  return s.n == d && s.h == (long long)N * d && s.b == (long long)H * N * d;
+}
+
+// Byte range spanned by a view (its bounding interval); -1 strides are rejected earlier.
+Range view_range(const void* p, fa_strides s, int B, int H, int N, int d, size_t elem) {
+  const long long last = (long long)(B - 1) * s.b + (long long)(H - 1) * s.h + (long long)(N - 1) * s.n + (d - 1);
+  return rng(p, (size_t)(last + 1) * elem);
+}
+
+fa_status check_general(int B, int H, int N, int d, float scale) {
+  if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+  if (d < 1 || d > kMaxGeneralD) return FA_ERR_UNSUPPORTED;
+  return check_sizes(B, H, N, padded_d(d), scale);
+}
+
+bool strides_ok(fa_strides s) { return s.b >= 0 && s.h >= 0 && s.n >= 0; }
+
+struct Carve {
+  char* p;
+  size_t off;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* r = reinterpret_cast<T*>(p + off);
+    off += align256(bytes);
+    return r;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_general_workspace_size(int B, int H, int N, int d) {
+  if (check_general(B, H, N, d, 1.0f) != FA_OK) return 0;
+  const size_t el = (size_t)B * H * N * padded_d(d);
+  return 3 * align256(el * 2) + align256(el * 4);
+}
+
+size_t fa_bwd_general_workspace_size(int B, int H, int N, int d, fa_bwd_variant variant) {
+  if (check_general(B, H, N, d, 1.0f) != FA_OK) return 0;
+  if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return 0;
+  const int dp = padded_d(d);
+  const size_t el = (size_t)B * H * N * dp;
+  return 4 * align256(el * 2) + 4 * align256(el * 4) + fa_bwd_workspace_size(B, H, N, dp, variant);
+}
+
+fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, int B, int H, int N, int d, int causal, float scale, float* o,
+                         fa_strides o_str, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_general(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  const fa_strides strs[] = {q_str, k_str, v_str, o_str};
+  for (const fa_strides& t : strs)
+    if (!strides_ok(t)) return FA_ERR_INVALID_ARG;
+  if (!aligned_to(q, 2) || !aligned_to(k, 2) || !aligned_to(v, 2) || !aligned_to(o, 4) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  const Range ro = view_range(o, o_str, B, H, N, d, 4), rl = rng(lse, (size_t)B * H * N * 4);
+  const Range ins[] = {view_range(q, q_str, B, H, N, d, 2), view_range(k, k_str, B, H, N, d, 2),
+                       view_range(v, v_str, B, H, N, d, 2)};
+  for (const Range& r : ins)
+    if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_INVALID_ARG;
+  if (overlaps(ro, rl)) return FA_ERR_INVALID_ARG;
+
+  const bool direct = supported_d(d) && contiguous(q_str, H, N, d) && contiguous(k_str, H, N, d) &&
+                      contiguous(v_str, H, N, d) && contiguous(o_str, H, N, d) && aligned16(q) && aligned16(k) &&
+                      aligned16(v) && aligned16(o);
+  if (direct) return fa_fwd_ex(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1);
+
+  const size_t need = fa_fwd_general_workspace_size(B, H, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  const Range rw = rng(workspace, need);
+  for (const Range& r : ins)
+    if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+  if (overlaps(ro, rw) || overlaps(rl, rw)) return FA_ERR_INVALID_ARG;
+
+  const int dp = padded_d(d);
+  const size_t el = (size_t)B * H * N * dp;
+  Carve c{static_cast<char*>(workspace), 0};
+  void* qp = c.take<char>(el * 2);
+  void* kp = c.take<char>(el * 2);
+  void* vp = c.take<char>(el * 2);
+  float* op = c.take<float>(el * 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fa::launch_gather_bf16(q, view_of(q_str), qp, B, H, N, d, dp, s);
+  fa::launch_gather_bf16(k, view_of(k_str), kp, B, H, N, d, dp, s);
+  fa::launch_gather_bf16(v, view_of(v_str), vp, B, H, N, d, dp, s);
+  fa_status st = launched();
+  if (st != FA_OK) return st;
+  st = fa_fwd_ex(qp, kp, vp, B, H, N, dp, causal, scale, op, lse, stream, -1);
+  if (st != FA_OK) return st;
+  fa::launch_scatter_f32(op, o, view_of(o_str), B, H, N, d, dp, s);
+  return launched();
+}
+
+fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, const float* o, fa_strides o_str, const float* lse, const void* dout,
+                         fa_strides dout_str, int B, int H, int N, int d, int causal, float scale,
+                         fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
+                         float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const fa_status sz = check_general(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return FA_ERR_UNSUPPORTED;
+  const fa_strides strs[] = {q_str, k_str, v_str, o_str, dout_str, dq_str, dk_str, dv_str};
+  for (const fa_strides& t : strs)
+    if (!strides_ok(t)) return FA_ERR_INVALID_ARG;
+  if (!aligned_to(q, 2) || !aligned_to(k, 2) || !aligned_to(v, 2) || !aligned_to(dout, 2) || !aligned_to(o, 4) ||
+      !aligned_to(dq, 4) || !aligned_to(dk, 4) || !aligned_to(dv, 4) || !aligned16(lse))
+    return FA_ERR_INVALID_ARG;
+  const Range ins[] = {view_range(q, q_str, B, H, N, d, 2),       view_range(k, k_str, B, H, N, d, 2),
+                       view_range(v, v_str, B, H, N, d, 2),       view_range(o, o_str, B, H, N, d, 4),
+                       view_range(dout, dout_str, B, H, N, d, 2), rng(lse, (size_t)B * H * N * 4)};
+  const Range outs[] = {view_range(dq, dq_str, B, H, N, d, 4), view_range(dk, dk_str, B, H, N, d, 4),
+                        view_range(dv, dv_str, B, H, N, d, 4)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : ins)
+      if (overlaps(outs[i], r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+  }
+
+  const bool direct = supported_d(d) && contiguous(q_str, H, N, d) && contiguous(k_str, H, N, d) &&
+                      contiguous(v_str, H, N, d) && contiguous(o_str, H, N, d) && contiguous(dout_str, H, N, d) &&
+                      contiguous(dq_str, H, N, d) && contiguous(dk_str, H, N, d) && contiguous(dv_str, H, N, d) &&
+                      aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dout) &&
+                      aligned16(dq) && aligned16(dk) && aligned16(dv);
+  if (direct)
+    return fa_bwd_ex(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace,
+                     workspace_bytes, stream, -1, -1);
+
+  const size_t need = fa_bwd_general_workspace_size(B, H, N, d, variant);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  const Range rw = rng(workspace, need);
+  for (const Range& r : ins)
+    if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+  for (const Range& r : outs)
+    if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+
+  const int dp = padded_d(d);
+  const size_t el = (size_t)B * H * N * dp;
+  Carve c{static_cast<char*>(workspace), 0};
+  void* qp = c.take<char>(el * 2);
+  void* kp = c.take<char>(el * 2);
+  void* vp = c.take<char>(el * 2);
+  void* dop = c.take<char>(el * 2);
+  float* op = c.take<float>(el * 4);
+  float* dqp = c.take<float>(el * 4);
+  float* dkp = c.take<float>(el * 4);
+  float* dvp = c.take<float>(el * 4);
+  const size_t inner = fa_bwd_workspace_size(B, H, N, dp, variant);
+  void* ws = c.take<char>(inner);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  fa::launch_gather_bf16(q, view_of(q_str), qp, B, H, N, d, dp, s);
+  fa::launch_gather_bf16(k, view_of(k_str), kp, B, H, N, d, dp, s);
+  fa::launch_gather_bf16(v, view_of(v_str), vp, B, H, N, d, dp, s);
+  fa::launch_gather_bf16(dout, view_of(dout_str), dop, B, H, N, d, dp, s);
+  fa::launch_gather_f32(o, view_of(o_str), op, B, H, N, d, dp, s);
+  fa_status st = launched();
+  if (st != FA_OK) return st;
+  st = fa_bwd_ex(qp, kp, vp, op, lse, dop, B, H, N, dp, causal, scale, variant, dqp, dkp, dvp, ws, inner, stream, -1,
+                 -1);
+  if (st != FA_OK) return st;
+  fa::launch_scatter_f32(dqp, dq, view_of(dq_str), B, H, N, d, dp, s);
+  fa::launch_scatter_f32(dkp, dk, view_of(dk_str), B, H, N, d, dp, s);
+  fa::launch_scatter_f32(dvp, dv, view_of(dv_str), B, H, N, d, dp, s);
+  return launched();
+}
+
+}  // extern "C"

@@ -65,4 +65,15 @@ const BwdConfig* dq_configs(int* count);           // 7-GEMM dQ
 
 int launch_preprocess(const PreArgs& a, int d, hipStream_t stream);
 
+// Element strides of a [B, H, N, d] view (the head dim is contiguous): element
+// (b, h, n, i) is at base[b * sb + h * sh + n * sn + i].
+struct View {
+  long long sb, sh, sn;
+};
+// General-entry layout adapters (fa_pad.hip): strided [B,H,N,d] view <-> contiguous
+// [B,H,N,dp] buffer; gathers zero-fill columns d .. dp-1.
+void launch_gather_bf16(const void* src, View s, void* dst, int B, int H, int N, int d, int dp, hipStream_t st);
+void launch_gather_f32(const float* src, View s, float* dst, int B, int H, int N, int d, int dp, hipStream_t st);
+void launch_scatter_f32(const float* src, float* dst, View s, int B, int H, int N, int d, int dp, hipStream_t st);
+
 }  // namespace fa

@@ -137,6 +137,45 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
                     fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
                     size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq);
 
+/* ---------------------------------------------------------------------------
+ * General entry points: any head dimension 1 <= d <= 256 and strided views.
+ *
+ * Every [B,H,N,d] tensor is described by its base pointer and element strides
+ * (b, h, n): element (b, h, n, i) is at base[b*stride.b + h*stride.h + n*stride.n + i]
+ * (the head dimension is contiguous; strides are >= 0).  lse stays contiguous
+ * [B,H,N].  Pointers need only element alignment (2 bytes for bf16, 4 for fp32;
+ * lse 16 bytes).  The math is that of fa_fwd / fa_bwd; the pages' kernels are
+ * built for fixed head dimensions, and issue 1172 asks for arbitrary head
+ * dimensions with strided rows, which these entries provide by running the fused
+ * kernels at Dp = the smallest of 64, 128, 256 that is >= d on zero-padded
+ * contiguous copies held in the workspace (zero columns change no score, so the
+ * result is the same attention), then writing the first d columns of the results
+ * into the caller's views.  When d is 64, 128 or 256 and every view is contiguous
+ * and 16-byte aligned, the call goes straight to fa_fwd / fa_bwd and needs only
+ * fa_bwd's workspace.
+ * Validation and errors as above; views that overlap an output are rejected
+ * (FA_ERR_INVALID_ARG), d outside 1..256 is FA_ERR_UNSUPPORTED. */
+typedef struct {
+  long long b, h, n;
+} fa_strides;
+
+/* Workspace bytes of the padded path (an upper bound for every call with these sizes). */
+size_t fa_fwd_general_workspace_size(int B, int H, int N, int d);
+size_t fa_bwd_general_workspace_size(int B, int H, int N, int d, fa_bwd_variant variant);
+
+/* Forward: q, k, v bf16 views; o fp32 view (written); lse fp32 [B,H,N] (written). */
+fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, int B, int H, int N, int d, int causal, float scale, float* o,
+                         fa_strides o_str, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward: q, k, v, dout bf16 views and o fp32 view (read), lse fp32 [B,H,N] (read);
+ * dq, dk, dv fp32 views (written). */
+fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, const float* o, fa_strides o_str, const float* lse, const void* dout,
+                         fa_strides dout_str, int B, int H, int N, int d, int causal, float scale,
+                         fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
+                         float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(fa_status s);
 

@@ -183,3 +183,60 @@ def test_report_tile_counts_match_brute_force():
     for N, rows, cols, causal, km in itertools.product([1, 33, 300, 2048], [64, 128, 256], [32, 64], [False, True],
                                                       [False, True]):
         assert tiles(N, rows, cols, causal, km) == walk(N, rows, cols, causal, km)
+
+
+def test_general_entries_validate_before_launching(L):
+    """Any head dim 1..256 and strided views: sizes of the padded workspace and the error paths (no
+    call here reaches a launch)."""
+    from exact_attention_102_amd import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
+    from exact_attention_102_amd.binding import FaStrides
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    B, H, N = 2, 3, 77
+    for d, dp in ((1, 64), (40, 64), (64, 64), (96, 128), (127, 128), (192, 256), (256, 256)):
+        el = B * H * N * dp
+        assert L.fa_fwd_general_workspace_size(B, H, N, d) == 3 * a256(2 * el) + a256(4 * el)
+        assert L.fa_bwd_general_workspace_size(B, H, N, d, 1) == 4 * a256(2 * el) + 4 * a256(4 * el) + a256(4 * B * H * N)
+    assert L.fa_fwd_general_workspace_size(B, H, N, 0) == 0
+    assert L.fa_fwd_general_workspace_size(B, H, N, 257) == 0
+    assert L.fa_bwd_general_workspace_size(B, H, N, 96, 5) == 0
+
+    d = 96
+    c = FaStrides(H * N * d, N * d, d)            # contiguous
+    t = FaStrides(N * H * d, d, H * d)            # a [B, N, H, d] tensor seen as [B, H, N, d]
+    ws_need = L.fa_fwd_general_workspace_size(B, H, N, d)
+
+    def gfwd(q=P, qs=t, o=P + 192 * MB, os_=c, lse=P + 256 * MB, ws=P + 512 * MB, wsb=ws_need, d=d, scale=0.1):
+        return L.fa_fwd_general(ctypes.c_void_p(q), qs, ctypes.c_void_p(P + 64 * MB), t, ctypes.c_void_p(P + 128 * MB),
+                                t, B, H, N, d, 1, scale, ctypes.c_void_p(o), os_, ctypes.c_void_p(lse),
+                                ctypes.c_void_p(ws), wsb, None)
+
+    assert gfwd(d=0) == FA_ERR_UNSUPPORTED
+    assert gfwd(d=257) == FA_ERR_UNSUPPORTED
+    assert gfwd(q=0) == FA_ERR_INVALID_ARG
+    assert gfwd(q=P + 1) == FA_ERR_INVALID_ARG                 # bf16 view on an odd byte address
+    assert gfwd(lse=P + 256 * MB + 4) == FA_ERR_INVALID_ARG    # lse must be 16-byte aligned
+    assert gfwd(qs=FaStrides(-1, d, H * d)) == FA_ERR_INVALID_ARG
+    assert gfwd(o=P + 8) == FA_ERR_INVALID_ARG                 # o overlaps q
+    assert gfwd(scale=float("nan")) == FA_ERR_INVALID_ARG
+    assert gfwd(ws=0) == FA_ERR_WORKSPACE
+    assert gfwd(wsb=ws_need - 1) == FA_ERR_WORKSPACE
+    assert gfwd(ws=P + 192 * MB + 256) == FA_ERR_INVALID_ARG   # workspace overlaps o
+
+    bneed = L.fa_bwd_general_workspace_size(B, H, N, d, 1)
+
+    def gbwd(variant=1, dq=P + 600 * MB, ws=P + 1024 * MB, wsb=bneed):
+        views = []
+        for i in range(4):   # q k v o
+            views += [ctypes.c_void_p(P + i * 64 * MB), t]
+        return L.fa_bwd_general(*views, ctypes.c_void_p(P + 320 * MB), ctypes.c_void_p(P + 384 * MB), t, B, H, N, d,
+                                0, 0.1, variant, ctypes.c_void_p(dq), c, ctypes.c_void_p(P + 700 * MB), c,
+                                ctypes.c_void_p(P + 800 * MB), c, ctypes.c_void_p(ws), wsb, None)
+
+    assert gbwd(variant=3) == FA_ERR_UNSUPPORTED
+    assert gbwd(ws=0) == FA_ERR_WORKSPACE
+    assert gbwd(wsb=bneed - 16) == FA_ERR_WORKSPACE
+    assert gbwd(dq=P + 700 * MB) == FA_ERR_INVALID_ARG         # dq overlaps dk
+    assert gbwd(dq=P + 64 * MB) == FA_ERR_INVALID_ARG          # dq overlaps k
