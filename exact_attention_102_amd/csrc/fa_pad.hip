@@ -9,7 +9,11 @@
 // every score q.k unchanged (so P, the softmax statistics and lse are exact), add
 // zero columns to O and dV, and add nothing to dQ and dK in the first d columns.
 // Both adapters are memory-bound and linear in N, against the fused kernels'
-// quadratic work.
+// quadratic work.  Each thread moves one 16-byte chunk of a padded row (8 bf16 or
+// 4 fp32 values): one vector access where the chunk is whole and 16-byte aligned in
+// the view, element accesses otherwise (ragged d, odd strides).
+#include <cstdint>
+
 #include "fa_launch.h"
 
 namespace fa {
@@ -17,37 +21,65 @@ namespace fa {
 namespace {
 
 constexpr int kPadThreads = 256;
-constexpr long long kPadMaxBlocks = 8192;
+constexpr long long kPadMaxBlocks = 16384;
 
-// (b, h, n) of flat row index `row` of a [B, H, N] grid, as an element offset in a view
-__device__ __forceinline__ long long view_row(long long row, int H, int N, const View& s) {
-  const long long n = row % N;
-  const long long bh = row / N;
-  return (bh / H) * s.sb + (bh % H) * s.sh + n * s.sn;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+
+// element offset in a view of flat row `row` of a [B, H, N] grid
+__device__ __forceinline__ long long view_row(int row, int H, int N, const View& s) {
+  const int n = row % N;
+  const int bh = row / N;
+  return (long long)(bh / H) * s.sb + (long long)(bh % H) * s.sh + (long long)n * s.sn;
 }
 
-template <typename T>
-__global__ void gather_kernel(const T* __restrict__ src, View s, T* __restrict__ dst, int H, int N, int d, int dp,
-                              long long total) {
+// T: element type; E: elements per 16-byte chunk
+template <typename T, int E>
+__global__ void gather_kernel(const T* __restrict__ src, View s, T* __restrict__ dst, int H, int N, int d,
+                              int chunks_log2, long long total_chunks) {
   const long long step = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
-    const int c = (int)(i % dp);
-    const long long row = i / dp;
-    T v = T(0);
-    if (c < d) v = src[view_row(row, H, N, s) + c];
-    dst[i] = v;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += step) {
+    const int row = (int)(i >> chunks_log2);
+    const int c0 = (int)(i & ((1 << chunks_log2) - 1)) * E;
+    const T* sp = src + view_row(row, H, N, s) + c0;
+    u32x4v v;
+    if (c0 + E <= d && (reinterpret_cast<uintptr_t>(sp) & 15u) == 0) {
+      v = *reinterpret_cast<const u32x4v*>(sp);
+    } else {
+      T tmp[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) tmp[e] = (c0 + e < d) ? sp[e] : T(0);
+      __builtin_memcpy(&v, tmp, 16);
+    }
+    *reinterpret_cast<u32x4v*>(dst + i * E) = v;
   }
 }
 
-template <typename T>
-__global__ void scatter_kernel(const T* __restrict__ src, T* __restrict__ dst, View s, int H, int N, int d, int dp,
-                               long long total) {
+template <typename T, int E>
+__global__ void scatter_kernel(const T* __restrict__ src, T* __restrict__ dst, View s, int H, int N, int d,
+                               int chunks_log2, long long total_chunks) {
   const long long step = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += step) {
-    const int c = (int)(i % d);
-    const long long row = i / d;
-    dst[view_row(row, H, N, s) + c] = src[row * dp + c];
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks; i += step) {
+    const int row = (int)(i >> chunks_log2);
+    const int c0 = (int)(i & ((1 << chunks_log2) - 1)) * E;
+    if (c0 >= d) continue;
+    T* dp = dst + view_row(row, H, N, s) + c0;
+    const u32x4v v = *reinterpret_cast<const u32x4v*>(src + i * E);
+    if (c0 + E <= d && (reinterpret_cast<uintptr_t>(dp) & 15u) == 0) {
+      *reinterpret_cast<u32x4v*>(dp) = v;
+    } else {
+      T tmp[E];
+      __builtin_memcpy(tmp, &v, 16);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (c0 + e < d) dp[e] = tmp[e];
+    }
   }
+}
+
+int log2_exact(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
 }
 
 unsigned pad_blocks(long long total) {
@@ -57,23 +89,26 @@ unsigned pad_blocks(long long total) {
 
 }  // namespace
 
+// dp is 64, 128 or 256, so a padded row holds a power-of-two number of chunks.
 void launch_gather_bf16(const void* src, View s, void* dst, int B, int H, int N, int d, int dp, hipStream_t st) {
-  const long long total = (long long)B * H * N * dp;
-  hipLaunchKernelGGL(gather_kernel<unsigned short>, dim3(pad_blocks(total)), dim3(kPadThreads), 0, st,
-                     static_cast<const unsigned short*>(src), s, static_cast<unsigned short*>(dst), H, N, d, dp,
-                     total);
+  const int cl = log2_exact(dp / 8);
+  const long long total = ((long long)B * H * N) << cl;
+  hipLaunchKernelGGL((gather_kernel<unsigned short, 8>), dim3(pad_blocks(total)), dim3(kPadThreads), 0, st,
+                     static_cast<const unsigned short*>(src), s, static_cast<unsigned short*>(dst), H, N, d, cl, total);
 }
 
 void launch_gather_f32(const float* src, View s, float* dst, int B, int H, int N, int d, int dp, hipStream_t st) {
-  const long long total = (long long)B * H * N * dp;
-  hipLaunchKernelGGL(gather_kernel<float>, dim3(pad_blocks(total)), dim3(kPadThreads), 0, st, src, s, dst, H, N, d,
-                     dp, total);
+  const int cl = log2_exact(dp / 4);
+  const long long total = ((long long)B * H * N) << cl;
+  hipLaunchKernelGGL((gather_kernel<float, 4>), dim3(pad_blocks(total)), dim3(kPadThreads), 0, st, src, s, dst, H, N,
+                     d, cl, total);
 }
 
 void launch_scatter_f32(const float* src, float* dst, View s, int B, int H, int N, int d, int dp, hipStream_t st) {
-  const long long total = (long long)B * H * N * d;
-  hipLaunchKernelGGL(scatter_kernel<float>, dim3(pad_blocks(total)), dim3(kPadThreads), 0, st, src, dst, s, H, N, d,
-                     dp, total);
+  const int cl = log2_exact(dp / 4);
+  const long long total = ((long long)B * H * N) << cl;
+  hipLaunchKernelGGL((scatter_kernel<float, 4>), dim3(pad_blocks(total)), dim3(kPadThreads), 0, st, src, dst, s, H,
+                     N, d, cl, total);
 }
 
 }  // namespace fa
