@@ -10,20 +10,26 @@ What is computed, and where the pages say so
   its time in elementwise passes over the N x N matrix -- masking, softmax and
   dropout -- and FlashAttention fuses them into the kernel.  Dropout here is the
   usual inverted dropout on the attention probabilities: each P_ij is kept with
-  probability 1 - p and scaled by 1 / (1 - p), otherwise zeroed.
+  probability 1 - p and scaled by the reciprocal of that probability, otherwise zeroed.
 * The pages give no random-number specification.  Reading (also in the design doc):
   the keep decision for score element (b, h, i, j) comes from the counter-based
   generator Philox4x32-10 of Salmon, Moraes, Dror and Shaw, "Parallel Random
   Numbers: As Easy as 1, 2, 3" (SC '11), so any kernel can recompute any
-  element's decision from its coordinates without storing a mask:
+  element's decision from its coordinates without storing a mask.  One call
+  yields 128 bits, read as eight 16-bit draws, one per key of an aligned group
+  of eight keys:
       key     = (seed mod 2^32, seed div 2^32)
-      counter = (j div 4, i, b * H + h, offset)
-      r       = word (j mod 4) of Philox4x32-10(counter, key)
-      keep    = r >= floor(p * 2^32)
-* Forward: O = (P * M / (1 - p)) V with M the keep mask; the log-sum-exp is that
-  of the undropped scores (dropout acts after the softmax normalisation).
-* Backward of L = sum(dO * O): with Pd = P * M / (1 - p),
-      dV = Pd^T dO,  dPd = dO V^T,  dP = dPd * M / (1 - p),
+      counter = (j div 8, i, b * H + h, offset)
+      draw    = 16-bit half (j mod 2) of word ((j mod 8) div 2), low half first
+      t       = floor(p * 2^16), at most 2^16 - 1
+      keep    = draw >= t
+  so the drop probability is t / 2^16 (p rounded down to a multiple of 2^-16)
+  and kept probabilities are scaled by s = 2^16 / (2^16 - t), the reciprocal of
+  the exact keep probability, which keeps O unbiased.
+* Forward: O = (P * M * s) V with M the keep mask; the log-sum-exp is that of
+  the undropped scores (dropout acts after the softmax normalisation).
+* Backward of L = sum(dO * O): with Pd = P * M * s,
+      dV = Pd^T dO,  dPd = dO V^T,  dP = dPd * M * s,
       dS = P * (dP - rowsum(P * dP)),  dQ = scale dS K,  dK = scale dS^T Q.
   rowsum(P * dP) = rowsum(Pd * dPd) = rowsum(dO * O), so the kernels' row term
   (computed from O and dO) is unchanged by dropout; the tests check that identity.
@@ -40,7 +46,7 @@ import numpy as np
 
 from .attention import _f64, score_matrix, softmax_rows
 
-__all__ = ["philox4x32_10", "keep_threshold", "dropout_keep_mask", "attention_forward_dropout",
+__all__ = ["philox4x32_10", "keep_threshold", "keep_scale", "dropout_keep_mask", "attention_forward_dropout",
            "attention_backward_dropout", "attention_forward_dropout_batched", "attention_backward_dropout_batched"]
 
 _M0 = np.uint64(0xD2511F53)
@@ -68,10 +74,15 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def keep_threshold(p: float) -> int:
-    """floor(p * 2^32) for a drop probability p in [0, 1): an element is kept iff its word >= this."""
+    """t = floor(p * 2^16), capped at 2^16 - 1, for p in [0, 1): an element is kept iff its draw >= t."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(np.floor(p * 4294967296.0)), 0xFFFFFFFF)
+    return min(int(np.floor(p * 65536.0)), 0xFFFF)
+
+
+def keep_scale(p: float) -> float:
+    """Factor on kept probabilities: 2^16 / (2^16 - t), the reciprocal of the keep probability."""
+    return 65536.0 / (65536 - keep_threshold(p))
 
 
 def dropout_keep_mask(bh: int, rows, n_keys: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
@@ -79,21 +90,21 @@ def dropout_keep_mask(bh: int, rows, n_keys: int, p: float, seed: int, offset: i
     rows = np.asarray(rows, dtype=np.int64)
     j = np.arange(n_keys, dtype=np.int64)
     ci = np.broadcast_to(rows[:, None], (rows.size, n_keys))
-    cj = np.broadcast_to(j[None, :] >> 2, (rows.size, n_keys))
+    cj = np.broadcast_to(j[None, :] >> 3, (rows.size, n_keys))
     words = philox4x32_10(cj, ci, np.int64(bh), np.int64(offset), seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
-    sel = np.broadcast_to(j[None, :] & 3, (rows.size, n_keys))
-    r = np.choose(sel, words)
-    return r >= np.uint32(keep_threshold(p))
+    word = np.choose(np.broadcast_to((j[None, :] & 7) >> 1, (rows.size, n_keys)), words)
+    draw = (word >> np.broadcast_to(16 * (j[None, :] & 1), (rows.size, n_keys)).astype(np.uint32)) & np.uint32(0xFFFF)
+    return draw >= np.uint32(keep_threshold(p))
 
 
 def attention_forward_dropout(q, k, v, scale: float, causal: bool, p: float, seed: int, offset: int = 0, bh: int = 0,
                               row_chunk: int = 256):
-    """One head (index bh): O = (P * M / (1 - p)) V and the undropped natural-log LSE."""
+    """One head (index bh): O = (P * M * s) V and the undropped natural-log LSE."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     n = q.shape[0]
     o = np.empty((n, v.shape[1]))
     lse = np.empty(n)
-    inv_keep = 1.0 / (1.0 - p)
+    inv_keep = keep_scale(p)
     for r0 in range(0, n, row_chunk):
         r1 = min(n, r0 + row_chunk)
         prob, l = softmax_rows(score_matrix(q[r0:r1], k, scale, causal, r0))
@@ -112,7 +123,7 @@ def attention_backward_dropout(q, k, v, do, scale: float, causal: bool, p: float
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     rowterm = np.empty(n)
-    inv_keep = 1.0 / (1.0 - p)
+    inv_keep = keep_scale(p)
     for r0 in range(0, n, row_chunk):
         r1 = min(n, r0 + row_chunk)
         prob, _ = softmax_rows(score_matrix(q[r0:r1], k, scale, causal, r0))

@@ -7,7 +7,7 @@
 * The gradients against central differences with the mask held fixed by the seed.
 * A pure-Python brute force of the masked forward on a tiny head.
 * Unbiasedness: the mean of the dropout forward over many seeds approaches the
-  undropped O (fails if the 1 / (1 - p) factor is missing or misplaced).
+  undropped O (fails if the keep-scale factor is missing or misplaced).
 * Keep-rate statistics, seed / offset / head / row / column decorrelation, and the
   row-term identity rowsum(P * dP) = rowsum(dO * O) that lets kernels keep their
   undropped row term.
@@ -19,7 +19,7 @@ import pytest
 
 from oracle import (attention_backward, attention_backward_dropout, attention_backward_dropout_batched,
                     attention_forward, attention_forward_dropout, attention_forward_dropout_batched,
-                    dropout_keep_mask, keep_threshold, philox4x32_10)
+                    dropout_keep_mask, keep_scale, keep_threshold, philox4x32_10)
 
 pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
 
@@ -52,24 +52,29 @@ def test_philox_vectorised_equals_scalar_calls():
 
 
 def test_keep_threshold_values():
-    assert keep_threshold(0.0) == 0
-    assert keep_threshold(0.5) == 1 << 31
-    assert keep_threshold(0.25) == 1 << 30
-    assert keep_threshold(1 - 2 ** -32) == 0xFFFFFFFF
+    assert keep_threshold(0.0) == 0 and keep_scale(0.0) == 1.0
+    assert keep_threshold(0.5) == 1 << 15 and keep_scale(0.5) == 2.0
+    assert keep_threshold(0.25) == 1 << 14
+    assert keep_threshold(0.1) == 6553 and keep_scale(0.1) == 65536 / (65536 - 6553)
+    assert keep_threshold(2 ** -17) == 0          # rounds down to "keep everything"
+    assert keep_threshold(1 - 2 ** -40) == 0xFFFF
     for bad in (-0.1, 1.0, 1.5):
         with pytest.raises(ValueError):
             keep_threshold(bad)
 
 
 def test_mask_follows_the_counter_layout():
-    """Element (i, j) of head bh is word (j mod 4) of Philox(j div 4, i, bh, offset; seed lo, seed hi)."""
+    """Element (i, j) of head bh is 16-bit half (j mod 2) of word ((j mod 8) div 2) of
+    Philox(j div 8, i, bh, offset; seed lo, seed hi), low half first."""
     seed, off, bh, p = 0x1234_5678_9ABC_DEF0, 3, 5, 0.3
-    m = dropout_keep_mask(bh, [0, 2, 9], 10, p, seed, off)
+    rows = [0, 2, 9]
+    m = dropout_keep_mask(bh, rows, 21, p, seed, off)
     t = keep_threshold(p)
-    for a, i in enumerate([0, 2, 9]):
-        for j in range(10):
-            w = philox4x32_10(j // 4, i, bh, off, seed & 0xFFFFFFFF, seed >> 32)[j % 4]
-            assert bool(m[a, j]) == (int(w) >= t)
+    for a, i in enumerate(rows):
+        for j in range(21):
+            w = int(philox4x32_10(j // 8, i, bh, off, seed & 0xFFFFFFFF, seed >> 32)[(j % 8) // 2])
+            draw = (w & 0xFFFF) if j % 2 == 0 else (w >> 16)
+            assert bool(m[a, j]) == (draw >= t)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -97,7 +102,8 @@ def test_dropout_forward_matches_brute_force(causal):
         keys = [j for j in range(9) if not causal or j <= i]
         s = [scale * sum(q[i, t] * k[j, t] for t in range(3)) for j in keys]
         z = sum(math.exp(x) for x in s)
-        w = [math.exp(x) / z * (1.0 / (1 - p) if mask[i, j] else 0.0) for x, j in zip(s, keys)]
+        w = [math.exp(x) / z * (65536 / (65536 - math.floor(p * 65536)) if mask[i, j] else 0.0)
+             for x, j in zip(s, keys)]
         for c in range(3):
             assert abs(o[i, c] - sum(w[a] * v[j, c] for a, j in enumerate(keys))) < 1e-13
         assert abs(lse[i] - math.log(z)) < 1e-13
@@ -148,7 +154,7 @@ def test_unbiased_over_seeds():
     se = runs.std(axis=0) / math.sqrt(S)
     z = np.abs(runs.mean(axis=0) - o_ref) / np.maximum(se, 1e-12)
     assert z.max() < 5.0, z.max()
-    # without the 1/(1-p) factor the mean would be (1-p) O: far outside that band
+    # without the keep-scale factor the mean would be (1-p) O: far outside that band
     assert np.abs(runs.mean(axis=0) * (1 - p) - o_ref).max() > 10 * se.max()
 
 
@@ -158,9 +164,9 @@ def test_keep_rate_and_decorrelation(p):
     m = dropout_keep_mask(3, np.arange(n), n, p, seed=0xDEADBEEF12345)
     sigma = math.sqrt(p * (1 - p) / m.size)
     assert abs(m.mean() - (1 - p)) < 5 * sigma
-    # each residue class of j (the four words of one Philox call) keeps at the same rate
-    for r in range(4):
-        sub = m[:, r::4]
+    # each residue class of j (the eight draws of one Philox call) keeps at the same rate
+    for r in range(8):
+        sub = m[:, r::8]
         assert abs(sub.mean() - (1 - p)) < 5 * math.sqrt(p * (1 - p) / sub.size)
     # other heads, seeds, offsets and the transposed coordinates give different masks that agree
     # only at the rate of independent draws: P(equal) = p^2 + (1-p)^2
