@@ -29,6 +29,11 @@ class FaStrides(ctypes.Structure):
     _fields_ = [("b", ctypes.c_longlong), ("h", ctypes.c_longlong), ("n", ctypes.c_longlong)]
 
 
+class FaDropout(ctypes.Structure):
+    """fa_dropout: drop probability p in [0, 1), 64-bit generator seed, 32-bit counter offset."""
+    _fields_ = [("p", ctypes.c_double), ("seed", ctypes.c_ulonglong), ("offset", ctypes.c_uint)]
+
+
 class FAError(RuntimeError):
     def __init__(self, status: int, what: str):
         super().__init__("%s: %s" % (what, fa_status_string(status)))
@@ -81,6 +86,13 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_general.argtypes = [vp, st, vp, st, vp, st, vp, st, vp, vp, st, i, i, i, i, i, f, i,
                                  vp, st, vp, st, vp, st, vp, sz, vp]
     L.fa_bwd_general.restype = i
+    dr = FaDropout
+    L.fa_fwd_dropout.argtypes = [vp, vp, vp, i, i, i, i, i, f, dr, vp, vp, vp]
+    L.fa_fwd_dropout.restype = i
+    L.fa_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, dr, i, vp, vp, vp, vp, sz, vp]
+    L.fa_bwd_dropout.restype = i
+    L.fa_dropout_keep_scale.argtypes = [ctypes.c_double]
+    L.fa_dropout_keep_scale.restype = ctypes.c_double
     _lib = L
     return L
 
@@ -140,8 +152,7 @@ def _check(t, name, dtype, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, cfg: int = -1):
-    """Forward: returns (o fp32 [B,H,N,d], lse fp32 [B,H,N]); allocates outputs if not given."""
+def _fwd_args(q, k, v, o, lse):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -155,15 +166,38 @@ def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, c
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     po = _check(o, "o", torch.float32, q.shape)
     pl = _check(lse, "lse", torch.float32, (B, H, N))
-    st = lib().fa_fwd_ex(pq, pk, pv, B, H, N, d, int(bool(causal)), float(scale), po, pl, _stream_ptr(stream), int(cfg))
+    return (B, H, N, d), (pq, pk, pv), (po, pl), (o, lse)
+
+
+def fa_fwd(q, k, v, causal: bool, scale: float, o=None, lse=None, stream=None, cfg: int = -1):
+    """Forward: returns (o fp32 [B,H,N,d], lse fp32 [B,H,N]); allocates outputs if not given."""
+    dims, ins, outs, res = _fwd_args(q, k, v, o, lse)
+    st = lib().fa_fwd_ex(*ins, *dims, int(bool(causal)), float(scale), *outs, _stream_ptr(stream), int(cfg))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
-    return o, lse
+    return res
 
 
-def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
-           dq=None, dk=None, dv=None, workspace=None, stream=None, cfg_dkdv: int = -1, cfg_dq: int = -1):
-    """Backward: returns (dq, dk, dv), fp32 [B,H,N,d]; allocates outputs/workspace if not given."""
+def fa_fwd_dropout(q, k, v, causal: bool, scale: float, p: float, seed: int, offset: int = 0, o=None, lse=None,
+                   stream=None):
+    """Forward with dropout on P (include/fa.h, fa_fwd_dropout): returns (o, lse)."""
+    dims, ins, outs, res = _fwd_args(q, k, v, o, lse)
+    drop = FaDropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF)
+    st = lib().fa_fwd_dropout(*ins, *dims, int(bool(causal)), float(scale), drop, *outs, _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_dropout")
+    return res
+
+
+def fa_dropout_keep_scale(p: float) -> float:
+    """Factor on kept probabilities for drop probability p (65536 / (65536 - floor(p 65536)))."""
+    r = lib().fa_dropout_keep_scale(float(p))
+    if r < 0:
+        raise ValueError("dropout probability must be in [0, 1)")
+    return r
+
+
+def _bwd_args(q, k, v, o, lse, dout, variant, dq, dk, dv, workspace):
     torch = _torch()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -183,11 +217,30 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().fa_bwd_ex(*ptr, B, H, N, d, int(bool(causal)), float(scale), int(variant), *pouts,
-                         ctypes.c_void_p(workspace.data_ptr()), ws_bytes, _stream_ptr(stream), int(cfg_dkdv), int(cfg_dq))
+    return (B, H, N, d), ptr, pouts, (ctypes.c_void_p(workspace.data_ptr()), ws_bytes), tuple(outs)
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
+           dq=None, dk=None, dv=None, workspace=None, stream=None, cfg_dkdv: int = -1, cfg_dq: int = -1):
+    """Backward: returns (dq, dk, dv), fp32 [B,H,N,d]; allocates outputs/workspace if not given."""
+    dims, ptr, pouts, ws, res = _bwd_args(q, k, v, o, lse, dout, variant, dq, dk, dv, workspace)
+    st = lib().fa_bwd_ex(*ptr, *dims, int(bool(causal)), float(scale), int(variant), *pouts, *ws,
+                         _stream_ptr(stream), int(cfg_dkdv), int(cfg_dq))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
-    return tuple(outs)
+    return res
+
+
+def fa_bwd_dropout(q, k, v, o, lse, dout, causal: bool, scale: float, p: float, seed: int, offset: int = 0,
+                   variant: int = FA_BWD_7GEMM, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward of the dropout forward (same p, seed, offset): returns (dq, dk, dv)."""
+    dims, ptr, pouts, ws, res = _bwd_args(q, k, v, o, lse, dout, variant, dq, dk, dv, workspace)
+    drop = FaDropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF)
+    st = lib().fa_bwd_dropout(*ptr, *dims, int(bool(causal)), float(scale), drop, int(variant), *pouts, *ws,
+                              _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dropout")
+    return res
 
 
 def fa_bwd_preprocess(o, dout, delta=None, dq=None, stream=None):

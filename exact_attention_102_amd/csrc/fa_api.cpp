@@ -96,6 +96,41 @@ fa_status launched() {
   return FA_OK;
 }
 
+// Dropout constants of one call: the 16-bit threshold t = floor(p * 2^16) (at most
+// 2^16 - 1) and the keep scale 2^16 / (2^16 - t); t == 0 runs the plain kernels.
+struct DropSpec {
+  unsigned k0 = 0, k1 = 0, offset = 0, t = 0;
+  float scale = 1.f;
+};
+
+bool drop_threshold(double p, unsigned* t) {
+  if (!std::isfinite(p) || p < 0.0 || p >= 1.0) return false;
+  const double f = std::floor(p * 65536.0);
+  *t = f >= 65535.0 ? 65535u : (unsigned)f;
+  return true;
+}
+
+fa_status drop_spec(const fa_dropout& d, DropSpec* out) {
+  unsigned t = 0;
+  if (!drop_threshold(d.p, &t)) return FA_ERR_INVALID_ARG;
+  out->k0 = (unsigned)(d.seed & 0xffffffffull);
+  out->k1 = (unsigned)(d.seed >> 32);
+  out->offset = d.offset;
+  out->t = t;
+  out->scale = (float)(65536.0 / (double)(65536u - t));
+  return FA_OK;
+}
+
+template <class Args>
+void set_drop(Args& a, const DropSpec* d) {
+  if (!d || d->t == 0) return;
+  a.drop_k0 = d->k0;
+  a.drop_k1 = d->k1;
+  a.drop_offset = d->offset;
+  a.drop_t = d->t;
+  a.drop_scale = d->scale;
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,8 +183,13 @@ int fa_default_config(int pass, int d, int causal) {
   return default_index(pass, d, causal);
 }
 
-fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
-                    float scale, float* o, float* lse, void* stream, int cfg) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd_ex, optionally with dropout (drop->t != 0: the dropout table's shape for d; cfg ignored).
+fa_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal, float scale,
+                   float* o, float* lse, void* stream, int cfg, const DropSpec* drop) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return FA_ERR_INVALID_ARG;
   const fa_status sz = check_sizes(B, H, N, d, scale);
@@ -161,9 +201,10 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, i
     if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_INVALID_ARG;
   if (overlaps(ro, rl)) return FA_ERR_INVALID_ARG;
 
+  const bool dropping = drop && drop->t != 0;
   int n = 0;
-  const FwdConfig* t = fwd_table(&n);
-  const int idx = cfg < 0 ? default_index(0, d, causal) : cfg;
+  const FwdConfig* t = dropping ? fa::fwd_dropout_configs(&n) : fwd_table(&n);
+  const int idx = dropping ? 0 : (cfg < 0 ? default_index(0, d, causal) : cfg);
   const int j = nth_for_d(t, n, d, idx);
   if (j < 0) return FA_ERR_UNSUPPORTED;
 
@@ -177,8 +218,32 @@ fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, i
   a.H = H;
   a.N = N;
   a.scale = scale;
+  set_drop(a, drop);
   if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                    float scale, float* o, float* lse, void* stream, int cfg) {
+  return fwd_impl(q, k, v, B, H, N, d, causal, scale, o, lse, stream, cfg, nullptr);
+}
+
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                         float scale, fa_dropout dropout, float* o, float* lse, void* stream) {
+  DropSpec ds;
+  const fa_status st = drop_spec(dropout, &ds);
+  if (st != FA_OK) return st;
+  return fwd_impl(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1, &ds);
+}
+
+double fa_dropout_keep_scale(double p) {
+  unsigned t = 0;
+  if (!drop_threshold(p, &t)) return -1.0;
+  return 65536.0 / (double)(65536u - t);
 }
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
@@ -296,9 +361,15 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   return launched();
 }
 
-fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
-                    int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
-                    float* dv, void* workspace, size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq) {
+}  // extern "C"
+
+namespace {
+
+// fa_bwd_ex, optionally with dropout (the dropout tables' shape for d; cfg_* ignored).
+fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                   int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                   float* dv, void* workspace, size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq,
+                   const DropSpec* drop) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
   for (const void* p : ptrs)
@@ -323,14 +394,17 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
   }
 
   const bool atomic = variant == FA_BWD_5GEMM_ATOMIC;
+  const bool dropping = drop && drop->t != 0;
   int n1 = 0, n3 = 0;
-  const BwdConfig* t1 = bwd_table(atomic ? 2 : 1, &n1);
-  const int i1 = nth_for_d(t1, n1, d, cfg_dkdv < 0 ? default_index(atomic ? 2 : 1, d, causal) : cfg_dkdv);
+  const BwdConfig* t1 = dropping ? (atomic ? fa::dkdv_atomic_dropout_configs(&n1) : fa::dkdv_dropout_configs(&n1))
+                                 : bwd_table(atomic ? 2 : 1, &n1);
+  const int i1 = nth_for_d(t1, n1, d,
+                           dropping ? 0 : (cfg_dkdv < 0 ? default_index(atomic ? 2 : 1, d, causal) : cfg_dkdv));
   if (i1 < 0) return FA_ERR_UNSUPPORTED;
-  const BwdConfig* t3 = bwd_table(3, &n3);
+  const BwdConfig* t3 = dropping ? fa::dq_dropout_configs(&n3) : bwd_table(3, &n3);
   int i3 = -1;
   if (!atomic) {
-    i3 = nth_for_d(t3, n3, d, cfg_dq < 0 ? default_index(3, d, causal) : cfg_dq);
+    i3 = nth_for_d(t3, n3, d, dropping ? 0 : (cfg_dq < 0 ? default_index(3, d, causal) : cfg_dq));
     if (i3 < 0) return FA_ERR_UNSUPPORTED;
   }
 
@@ -346,12 +420,35 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
   fa_status st = launched();
   if (st != FA_OK) return st;
 
-  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv);
+  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv);
+  set_drop(a, drop);
   if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   st = launched();
   if (st != FA_OK || atomic) return st;
   if (t3[i3].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                    int B, int H, int N, int d, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                    float* dv, void* workspace, size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq) {
+  return bwd_impl(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace, workspace_bytes,
+                  stream, cfg_dkdv, cfg_dq, nullptr);
+}
+
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dout, int B, int H, int N, int d, int causal, float scale, fa_dropout dropout,
+                         fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  DropSpec ds;
+  const fa_status st = drop_spec(dropout, &ds);
+  if (st != FA_OK) return st;
+  return bwd_impl(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace, workspace_bytes,
+                  stream, -1, -1, &ds);
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,

@@ -9,7 +9,14 @@
 // c = scale * log2 e; dP = dO V^T; dS = P * (dP - delta_i) where delta_i =
 // sum_k dO_ik O_ik (the preprocess kernel); dV = P^T dO; dK = scale * dS^T Q;
 // dQ = scale * dS K.
+//
+// DROP: dropout on P (fa_dropout.h).  With M the keep mask and s the keep scale,
+// the forward used Pd = P * M * s, so dV = Pd^T dO and dP = (dO V^T) * M * s, while
+// dS = P * (dP - delta_i) keeps its form: delta_i = rowsum(Pd * dO V^T) =
+// rowsum(dO * O) is still what the preprocess kernel computes.  The kernels redraw
+// the forward's mask from the same counters.
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -108,7 +115,7 @@ struct RowStager {
 // (query block, d block) pairs) and adds it to dq with fp32 atomics, one atomic
 // per dq element per workgroup and query tile.
 // KV_LDS keeps the workgroup's K and V in LDS instead of registers (large d).
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS>
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DROP>
 struct DkdvMath {
   // K tile: plain row fragments (KV_LDS) and/or transposed reads (atomic dQ product)
   static constexpr int KMODE = ATOMIC ? (KV_LDS ? kBoth : kColOnly) : kRowOnly;
@@ -127,7 +134,7 @@ struct DkdvMath {
                                               float c, float scale, const RowOffsets<D, kBoth>& fr,
                                               const ColOffsets<D, kBoth>& fc, const RowOffsets<D, KMODE>& pk,
                                               const RowOffsets<D, kRowOnly>& pv, int wave, int g, int l32,
-                                              int lane) {
+                                              int lane, const DropCtx& dc, float ks) {
     const LDS float* l2t = stats;
     const LDS float* dlt = stats + BQ;
 #pragma unroll
@@ -139,6 +146,14 @@ struct DkdvMath {
       // Blocks wholly past the end (padding rows, P = 0), or wholly above the causal
       // diagonal for this wave's keys, contribute nothing.
       if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
+        // draws of this lane's key for queries qbase + 16 h + 8 g + (0..7): lane t of
+        // each 8-lane key group draws query ... + t for the whole group, then transpose
+        u32x4 dr[DROP ? 2 : 1];
+        if constexpr (DROP) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            dr[h] = transpose8_b16(drop_draws(dc, (kw >> 3) + (l32 >> 3), qbase + 16 * h + 8 * g + (l32 & 7)), lane);
+        }
         f32x16 s = zero16(), dp = zero16();
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
@@ -197,9 +212,15 @@ struct DkdvMath {
             if (key > q) pv = 0.f;
           }
           p[r] = pv;
-          ds[r] = pv * (dp[r] - dl[r]);
+          float dpv = dp[r];
+          if constexpr (DROP) dpv = drop_keep(dr[r >> 3], r & 7, dc.t) ? dpv * ks : 0.f;
+          ds[r] = pv * (dpv - dl[r]);
         }
-        const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+        bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+        if constexpr (DROP) {  // dV takes Pd = P * M * s; s is applied when dV is stored
+          pb0 = drop_mask8(pb0, dr[0], dc.t);
+          pb1 = drop_mask8(pb1, dr[1], dc.t);
+        }
         bf16x8 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -269,9 +290,9 @@ struct DkdvMath {
 
 // DEFER (atomic only): the dQ product and atomics of a query tile run at the start
 // of the next tile, from a second dS^T buffer, instead of behind an extra barrier.
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER>
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER, bool DROP>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
-  using M = DkdvMath<D, BQ, NW, CAUSAL, ATOMIC, KV_LDS>;
+  using M = DkdvMath<D, BQ, NW, CAUSAL, ATOMIC, KV_LDS, DROP>;
   constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
   constexpr int NT = NW * 64;
   constexpr int QTILE = BQ * D * 2;
@@ -321,6 +342,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const float* delh = a.delta + (size_t)bh * N;
   float* dqh = ATOMIC ? a.dq + head : nullptr;
   const float c = a.scale * kLog2e;
+  const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
+  const float ks = a.drop_scale;
 
   const int k0 = kt * BK;
   const int kw = k0 + wave * 32;
@@ -391,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
     }
     M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst0, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
-            pk, pv, wave, g, l32, lane);
+            pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
       M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
@@ -414,7 +437,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     }
     if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, DEFER ? dst1 : dst0, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N,
-            c, a.scale, fr, fc, pk, pv, wave, g, l32, lane);
+            c, a.scale, fr, fc, pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
       M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane);
@@ -431,6 +454,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   if (key < N) {
     float* dkr = a.dk + head + (size_t)key * D;
     float* dvr = a.dv + head + (size_t)key * D;
+    const float vs = DROP ? ks : 1.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -438,7 +462,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
         const int col = db * 32 + 8 * a4 + 4 * g;
         const f32x4 kv = {dk[db][4 * a4] * a.scale, dk[db][4 * a4 + 1] * a.scale, dk[db][4 * a4 + 2] * a.scale,
                           dk[db][4 * a4 + 3] * a.scale};
-        const f32x4 vv = {dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
+        const f32x4 vv = {dv[db][4 * a4] * vs, dv[db][4 * a4 + 1] * vs, dv[db][4 * a4 + 2] * vs,
+                          dv[db][4 * a4 + 3] * vs};
         *(f32x4*)(dkr + col) = kv;
         *(f32x4*)(dvr + col) = vv;
       }
@@ -455,7 +480,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T                 A = transposed reads of the K tile
 // No atomics: each dq element is written once, so results are reproducible bit
 // for bit (issue 1172: the 7-GEMM form is deterministic).
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool DROP>
 struct DqMath {
   static constexpr int KB = BC / 32;
   static constexpr int DB = D / 32;
@@ -464,8 +489,15 @@ struct DqMath {
                                               const bf16x8 (&dof)[KK], f32x16 (&dq)[DB], float lse2, float dl,
                                               int k0, int q_w, int qi, int N, float c,
                                               const RowOffsets<D, kBoth>& fkr, const ColOffsets<D, kBoth>& fkc,
-                                              const RowOffsets<D, kRowOnly>& fvr, int g) {
+                                              const RowOffsets<D, kRowOnly>& fvr, int g, const DropCtx& dc,
+                                              float ks) {
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w);
+    // draws of keys k0 + 32 kb + 16 h + 8 g + (0..7) for this lane's query
+    u32x4 dr[DROP ? 2 * KB : 1];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int i = 0; i < 2 * KB; ++i) dr[i] = drop_draws(dc, ((k0 + 8 * g) >> 3) + 2 * i, qi);
+    }
     bf16x8 dsb[2 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -484,7 +516,9 @@ struct DqMath {
           const int kidx = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
           if (kidx >= N || (CAUSAL && kidx > qi)) pv = 0.f;
         }
-        ds[r] = pv * (dp[r] - dl);
+        float dpv = dp[r];
+        if constexpr (DROP) dpv = drop_keep(dr[2 * kb + (r >> 3)], r & 7, dc.t) ? dpv * ks : 0.f;
+        ds[r] = pv * (dpv - dl);
       }
       dsb[2 * kb] = pack8(ds, 0);
       dsb[2 * kb + 1] = pack8(ds, 8);
@@ -497,9 +531,9 @@ struct DqMath {
   }
 };
 
-template <int D, int BC, int NW, int OCC, bool CAUSAL>
+template <int D, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
-  using M = DqMath<D, BC, CAUSAL>;
+  using M = DqMath<D, BC, CAUSAL, DROP>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;
   constexpr int DB = M::DB, KK = M::KK;
@@ -531,6 +565,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   const __bf16* Vh = a.v + head;
   const __bf16* dOh = a.dout + head;
   const float c = a.scale * kLog2e;
+  const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
 
   const int q_wg = qt * BR;
   const int q_w = q_wg + wave * 32;
@@ -578,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     }
     // waves wholly past the end (padding rows) or below this key tile's diagonal skip the tile
     if (q_w < N && (!CAUSAL || j * BC <= q_w + 31))
-      M::step(kbuf0, vbuf0, qf, dof, dq, lse2, dl, j * BC, q_w, qi, N, c, fkr, fkc, fvr, g);
+      M::step(kbuf0, vbuf0, qf, dof, dq, lse2, dl, j * BC, q_w, qi, N, c, fkr, fkc, fvr, g, dc, a.drop_scale);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
@@ -592,7 +627,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
       vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (q_w < N && (!CAUSAL || (j + 1) * BC <= q_w + 31))
-      M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fkr, fkc, fvr, g);
+      M::step(kbuf1, vbuf1, qf, dof, dq, lse2, dl, (j + 1) * BC, q_w, qi, N, c, fkr, fkc, fvr, g, dc, a.drop_scale);
     wait_tile();
     __syncthreads();
   }
@@ -612,32 +647,35 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false>
+template <int D, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false, bool DROP = false>
 static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 32 * NW;
   const int nkt = (a.N + BK - 1) / BK;
   const long long blocks = (long long)a.B * a.H * nkt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+  if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, true, ATOMIC, KV_LDS, DEFER>), dim3((unsigned)blocks), dim3(NW * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, true, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+                       dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, false, ATOMIC, KV_LDS, DEFER>), dim3((unsigned)blocks), dim3(NW * 64),
-                       0, stream, a);
+    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, false, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+                       dim3(NW * 64), 0, stream, a);
   }
   return 0;
 }
 
-template <int D, int BC, int NW, int OCC>
+template <int D, int BC, int NW, int OCC, bool DROP = false>
 static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.H * nqt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+  if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
   }
   return 0;
 }
@@ -653,6 +691,18 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   }
 #define DQ_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC> }
+#define DKDV_DROP_CFG(D, BQ, NW, KVL)                                                                   \
+  {                                                                                                       \
+    D, 32 * (NW), BQ, NW, "dkdv+dropout d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                     \
+        &launch_dkdv<D, BQ, NW, false, KVL, false, true>                                                  \
+  }
+#define DKDVA_DROP_CFG(D, BQ, NW, KVL, DEF)                                                             \
+  {                                                                                                       \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " defer" #DEF, \
+        &launch_dkdv<D, BQ, NW, true, KVL, DEF, true>                                                     \
+  }
+#define DQ_DROP_CFG(D, BC, NW, OCC) \
+  { D, 32 * (NW), BC, NW, "dq+dropout d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC, true> }
 
 const BwdConfig* dkdv_configs(int* count) {
   static const BwdConfig table[] = {
@@ -681,6 +731,32 @@ const BwdConfig* dq_configs(int* count) {
       DQ_CFG(64, 64, 4, 2),  DQ_CFG(64, 128, 4, 2), DQ_CFG(64, 64, 8, 2),
       DQ_CFG(128, 64, 4, 2), DQ_CFG(128, 32, 4, 2), DQ_CFG(128, 64, 8, 2),
       DQ_CFG(256, 32, 4, 1), DQ_CFG(256, 64, 4, 1),
+  };
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+// Dropout: the non-causal default shape of each head dim.
+const BwdConfig* dkdv_dropout_configs(int* count) {
+  static const BwdConfig table[] = {
+      DKDV_DROP_CFG(64, 64, 8, false), DKDV_DROP_CFG(128, 64, 4, false), DKDV_DROP_CFG(256, 32, 2, true),
+  };
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+const BwdConfig* dkdv_atomic_dropout_configs(int* count) {
+  static const BwdConfig table[] = {
+      DKDVA_DROP_CFG(64, 64, 4, false, false), DKDVA_DROP_CFG(128, 64, 4, false, false),
+      DKDVA_DROP_CFG(256, 32, 2, true, false),
+  };
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+const BwdConfig* dq_dropout_configs(int* count) {
+  static const BwdConfig table[] = {
+      DQ_DROP_CFG(64, 64, 4, 2), DQ_DROP_CFG(128, 64, 8, 2), DQ_DROP_CFG(256, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -24,14 +24,20 @@
 // that the PV product actually consumes (one v_dot2c_f32_bf16 per pair).  O is
 // divided by l~, so a row whose softmax is one-hot returns exactly that V row
 // even when its dominant P is not a power of two; lse = ln(2) * (m + log2 l).
+//
+// DROP: dropout on P (fa_dropout.h).  The statistics m, l, l~ and lse stay those of
+// the undropped P; the bf16 P^T fed to the PV product has its dropped entries
+// zeroed, and the final O / l~ is multiplied by the keep scale.  The draws of a
+// tile depend only on indices, so they are made before the tile's products.
 #include "fa_device.h"
+#include "fa_dropout.h"
 #include "fa_launch.h"
 
 namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int BC, bool CAUSAL>
+template <int D, int BC, bool CAUSAL, bool DROP>
 struct FwdTileMath {
   static constexpr int KB = BC / 32;  // 32-key blocks per tile
   static constexpr int DB = D / 32;   // 32-wide blocks of the head dim
@@ -43,7 +49,13 @@ struct FwdTileMath {
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               f32x16 (&o)[DB], float& m_run, float& l_run, float& lb_run, int k0,
                                               int q_w, int qi, int N, float c, const RowOffsets<D, kRowOnly>& fk,
-                                              const ColOffsets<D, kColOnly>& fv, int g) {
+                                              const ColOffsets<D, kColOnly>& fv, int g, const DropCtx& dc) {
+    // draws of keys k0 + 32 kb + 16 h + 8 g + (0..7) for this lane's query
+    u32x4 dr[DROP ? 2 * KB : 1];
+    if constexpr (DROP) {
+#pragma unroll
+      for (int ks = 0; ks < 2 * KB; ++ks) dr[ks] = drop_draws(dc, ((k0 + 8 * g) >> 3) + 2 * ks, qi);
+    }
     f32x16 s[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
@@ -108,6 +120,10 @@ struct FwdTileMath {
       pb[2 * kb + 1] = pack8(s[kb], 8);
       rb = sum_bf16x8(pb[2 * kb], rb);
       rb = sum_bf16x8(pb[2 * kb + 1], rb);
+      if constexpr (DROP) {
+        pb[2 * kb] = drop_mask8(pb[2 * kb], dr[2 * kb], dc.t);
+        pb[2 * kb + 1] = drop_mask8(pb[2 * kb + 1], dr[2 * kb + 1], dc.t);
+      }
     }
     l_run += rs;
     lb_run += rb;
@@ -129,9 +145,9 @@ struct FwdTileMath {
 
 // OCC: waves per SIMD the register allocation must allow (2 lets a second wave's
 // MFMAs overlap this wave's softmax; d = 256 needs the whole register file).
-template <int D, int BC, int NW, int OCC, bool CAUSAL>
+template <int D, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
-  using M = FwdTileMath<D, BC, CAUSAL>;
+  using M = FwdTileMath<D, BC, CAUSAL, DROP>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;  // bytes of one K or V tile
   constexpr int DB = M::DB, KK = M::KK;
@@ -162,6 +178,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const __bf16* Kh = a.k + head;
   const __bf16* Vh = a.v + head;
   const float c = a.scale * kLog2e;
+  const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
 
   const int q_wg = qt * BR;
   const int q_w = q_wg + wave * 32;
@@ -202,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       vdma.issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     if (!CAUSAL || j * BC <= q_w + 31)
-      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g);
+      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g, dc);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
@@ -215,13 +232,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (!CAUSAL || (j + 1) * BC <= q_w + 31)
-      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g);
+      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g, dc);
     wait_tile();
     __syncthreads();
   }
 
   const float lt = half_swap_sum(l_run);
-  const float inv = 1.f / half_swap_sum(lb_run);
+  const float inv = (DROP ? a.drop_scale : 1.f) / half_swap_sum(lb_run);
   if (qi < N) {
     float* orow = a.o + head + (size_t)qi * D;
 #pragma unroll
@@ -237,22 +254,27 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int BC, int NW, int OCC>
+template <int D, int BC, int NW, int OCC, bool DROP = false>
 static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
   const long long blocks = (long long)a.B * a.H * nqt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+  if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
   }
   return 0;
 }
 
 #define FWD_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "fwd d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, BC, NW, OCC> }
+#define FWD_DROP_CFG(D, BC, NW, OCC) \
+  { D, 32 * (NW), BC, NW, "fwd+dropout d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, BC, NW, OCC, true> }
 
 // Host-side table (function-local so that only the host pass materialises it).
 const FwdConfig* fwd_configs(int* count) {
@@ -260,6 +282,14 @@ const FwdConfig* fwd_configs(int* count) {
       FWD_CFG(64, 64, 4, 2),   FWD_CFG(64, 128, 4, 2),  FWD_CFG(64, 64, 8, 2),  FWD_CFG(64, 128, 8, 2),
       FWD_CFG(128, 64, 4, 2),  FWD_CFG(128, 32, 4, 2),  FWD_CFG(128, 64, 8, 2), FWD_CFG(128, 128, 4, 1),
       FWD_CFG(256, 32, 4, 1),  FWD_CFG(256, 64, 4, 1),
+  };
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+const FwdConfig* fwd_dropout_configs(int* count) {
+  static const FwdConfig table[] = {
+      FWD_DROP_CFG(64, 64, 8, 2), FWD_DROP_CFG(128, 64, 4, 2), FWD_DROP_CFG(256, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -13,6 +13,9 @@ struct FwdArgs {
   float* lse;
   int B, H, N;
   float scale;
+  // dropout on P (fa_dropout.h); drop_t == 0 means none
+  unsigned drop_k0 = 0, drop_k1 = 0, drop_offset = 0, drop_t = 0;
+  float drop_scale = 1.f;
 };
 
 struct BwdArgs {
@@ -27,6 +30,8 @@ struct BwdArgs {
   float* dv;
   int B, H, N;
   float scale;
+  unsigned drop_k0 = 0, drop_k1 = 0, drop_offset = 0, drop_t = 0;
+  float drop_scale = 1.f;
 };
 
 struct PreArgs {
@@ -62,6 +67,11 @@ const FwdConfig* fwd_configs(int* count);
 const BwdConfig* dkdv_configs(int* count);         // 7-GEMM dK/dV (no dQ)
 const BwdConfig* dkdv_atomic_configs(int* count);  // 5-GEMM dK/dV with fp32-atomic dQ
 const BwdConfig* dq_configs(int* count);           // 7-GEMM dQ
+// The same passes with dropout on P: one configuration per head dim each.
+const FwdConfig* fwd_dropout_configs(int* count);
+const BwdConfig* dkdv_dropout_configs(int* count);
+const BwdConfig* dkdv_atomic_dropout_configs(int* count);
+const BwdConfig* dq_dropout_configs(int* count);
 
 int launch_preprocess(const PreArgs& a, int d, hipStream_t stream);
 

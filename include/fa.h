@@ -176,6 +176,44 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
                          fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
                          float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Dropout on the attention probabilities, fused into the kernels.
+ *
+ * Dropout is one of the elementwise passes over the N x N matrix that unfused
+ * attention spends its time on ("ELI5: FlashAttention", standard-attention
+ * highlights); here it runs inside the fused kernels and its mask never reaches
+ * memory.  The pages fix no random-number generator; this library draws the keep
+ * decision of element (b, h, i, j) (query i, key j) from Philox4x32-10 (Salmon,
+ * Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC '11):
+ *   key      (seed & 0xffffffff, seed >> 32)
+ *   counter  (j / 8, i, b * H + h, offset)
+ *   draw     16-bit half (j % 2) of output word (j % 8) / 2, low half first
+ *   keep     draw >= t, t = floor(p * 65536) capped at 65535
+ * so the drop probability is t / 65536 (p rounded down to a multiple of 2^-16);
+ * kept probabilities are scaled by 65536 / (65536 - t), the reciprocal of the keep
+ * probability (fa_dropout_keep_scale), so E[o] is the undropped output.
+ * The forward computes o = (P * M * s) v with lse that of the undropped scores;
+ * the backward gives the gradients of sum(dout * o) for that same mask, redrawn
+ * from (seed, offset): pass the forward's values.  A p that rounds to t = 0 runs the
+ * plain kernels.  Head dims 64, 128, 256; each pass runs one tile shape per head dim.
+ * Errors as above; p outside [0, 1) or not finite is FA_ERR_INVALID_ARG. */
+typedef struct {
+  double p;                /* drop probability, 0 <= p < 1                           */
+  unsigned long long seed; /* generator key                                          */
+  unsigned offset;         /* fourth counter word (e.g. a step or layer index)       */
+} fa_dropout;
+/* Forward with dropout: arguments and outputs as fa_fwd. */
+fa_status fa_fwd_dropout(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal,
+                         float scale, fa_dropout dropout, float* o, float* lse, void* stream);
+/* Backward with dropout: arguments, outputs and workspace as fa_bwd; o and lse are the
+ * dropout forward's, dropout must equal the forward's. */
+fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dout, int B, int H, int N, int d, int causal, float scale, fa_dropout dropout,
+                         fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
+                         size_t workspace_bytes, void* stream);
+/* The factor kept probabilities are scaled by for drop probability p: 65536 / (65536 - t);
+ * -1 if p is outside [0, 1). */
+double fa_dropout_keep_scale(double p);
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(fa_status s);
 

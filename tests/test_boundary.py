@@ -240,3 +240,42 @@ def test_general_entries_validate_before_launching(L):
     assert gbwd(wsb=bneed - 16) == FA_ERR_WORKSPACE
     assert gbwd(dq=P + 700 * MB) == FA_ERR_INVALID_ARG         # dq overlaps dk
     assert gbwd(dq=P + 64 * MB) == FA_ERR_INVALID_ARG          # dq overlaps k
+
+
+def test_dropout_entries_validate_and_keep_scale(L):
+    """Dropout entry points: the keep scale is the oracle's 2^16 / (2^16 - floor(p 2^16)); p outside
+    [0, 1), bad sizes and bad pointers are rejected before any launch."""
+    from oracle import keep_scale
+
+    from exact_attention_102_amd import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
+    from exact_attention_102_amd.binding import FaDropout
+    for p in (0.0, 1e-9, 0.1, 0.25, 0.5, 0.9, 1 - 2 ** -20):
+        assert L.fa_dropout_keep_scale(p) == keep_scale(p)
+    for p in (-0.5, 1.0, 2.0, float("nan"), float("inf")):
+        assert L.fa_dropout_keep_scale(p) == -1.0
+
+    B, H, N, d = 2, 3, 100, 64
+
+    def dfwd(p=0.1, d=d, q=P, o=P + 64 * MB):
+        return L.fa_fwd_dropout(ctypes.c_void_p(q), ctypes.c_void_p(P + 16 * MB), ctypes.c_void_p(P + 32 * MB), B, H,
+                                N, d, 0, 0.125, FaDropout(p, 1234, 5), ctypes.c_void_p(o),
+                                ctypes.c_void_p(P + 128 * MB), None)
+
+    assert dfwd(p=-0.1) == FA_ERR_INVALID_ARG
+    assert dfwd(p=1.0) == FA_ERR_INVALID_ARG
+    assert dfwd(p=float("nan")) == FA_ERR_INVALID_ARG
+    assert dfwd(d=96) == FA_ERR_UNSUPPORTED
+    assert dfwd(q=0) == FA_ERR_INVALID_ARG
+    assert dfwd(o=P + 8) == FA_ERR_INVALID_ARG         # o overlaps q
+    need = L.fa_bwd_workspace_size(B, H, N, d, 1)
+
+    def dbwd(p=0.1, variant=1, ws=P + 1024 * MB, wsb=need):
+        ins = [ctypes.c_void_p(P + i * 16 * MB) for i in range(6)]
+        return L.fa_bwd_dropout(*ins, B, H, N, d, 1, 0.125, FaDropout(p, 99, 0), variant,
+                                ctypes.c_void_p(P + 256 * MB), ctypes.c_void_p(P + 320 * MB),
+                                ctypes.c_void_p(P + 384 * MB), ctypes.c_void_p(ws), wsb, None)
+
+    assert dbwd(p=1.5) == FA_ERR_INVALID_ARG
+    assert dbwd(variant=7) == FA_ERR_UNSUPPORTED
+    assert dbwd(ws=0) == FA_ERR_WORKSPACE
+    assert dbwd(wsb=need - 16) == FA_ERR_WORKSPACE
