@@ -279,3 +279,17 @@ def test_dropout_entries_validate_and_keep_scale(L):
     assert dbwd(variant=7) == FA_ERR_UNSUPPORTED
     assert dbwd(ws=0) == FA_ERR_WORKSPACE
     assert dbwd(wsb=need - 16) == FA_ERR_WORKSPACE
+
+
+def test_traffic_classifies_kernel_names():
+    """The counter summary keys kernels by pass and mask from their template arguments."""
+    from exact_attention_102_amd.traffic import classify
+    assert classify("void fa::fwd_kernel<128, 64, 4, 2, true, false>(fa::FwdArgs)") == ("fwd", "causal")
+    assert classify("void fa::fwd_kernel<64, 64, 8, 2, false, false>(fa::FwdArgs)") == ("fwd", "full")
+    assert classify("void fa::dq_kernel<128, 64, 8, 2, false, false>(fa::BwdArgs)") == ("dq", "full")
+    assert classify("void fa::dkdv_kernel<128, 64, 4, true, true, false, false, false>(fa::BwdArgs)") == \
+        ("dkdv_atomic", "causal")
+    assert classify("void fa::dkdv_kernel<128, 64, 4, false, false, true, false, false>(fa::BwdArgs)") == \
+        ("dkdv", "full")
+    assert classify("void fa::fwd_kernel<128, 64, 4, 2, false, true>(fa::FwdArgs)") is None   # dropout
+    assert classify("void fa::preprocess_kernel<128>(fa::PreArgs)") == ("preprocess", None)
