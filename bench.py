@@ -73,6 +73,34 @@ def stored_traffic(kernel: str, mask: str, workload: str):
     return ent.get("bytes_per_launch")
 
 
+def atomic_adds_per_launch(B, H, N, d, causal, bk, bq):
+    """fp32 atomic adds one launch of the fused dK/dV + dQ kernel issues: for each (key tile, visited
+    query tile) pair, one add per dq element of the query tile's rows inside the sequence."""
+    nkt, nqt = -(-N // bk), -(-N // bq)
+    rows = 0
+    for kt in range(nkt):
+        q_first = (kt * bk) // bq if causal else 0
+        for qt in range(q_first, nqt):
+            rows += min(N, (qt + 1) * bq) - qt * bq
+    return B * H * rows * d
+
+
+def atomic_ceiling(w):
+    """fp32 atomics per second that the committed probe summary measured for this shape, or None."""
+    path = os.path.join(ROOT, "profiles", "atomic_dq_probe.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("{"):
+                continue
+            rec = json.loads(line)
+            if rec.get("probe") == "fp32 atomic add" and (rec["B"], rec["H"], rec["N"], rec["d"]) == (w.B, w.H, w.N,
+                                                                                                     w.d):
+                return rec["G_per_s"]
+    return None
+
+
 def cpu_baseline(w, causal_modes, heads):
     """The fp64 oracle as it stands, timed on this host's cores over `heads` heads of the workload."""
     from threadpoolctl import threadpool_limits
@@ -221,6 +249,16 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "%s (%s mask)" % (kn, mname), "launch_ms": round(t_ms, 4),
                 "flops_per_launch": kflops}
+    if kn == "dkdv_atomic":
+        # the fused dQ atomics, not the MFMAs, bound this kernel: its rate against the probe's ceiling
+        from exact_attention_102_amd.report import tile_shape
+        bk, bq = tile_shape(fa_config_name(2, d, mname == "causal", fa_default_config(2, d, mname == "causal")))
+        adds = atomic_adds_per_launch(B, H, N, d, mname == "causal", bk, bq)
+        rate = adds / (t_ms * 1e-3) / 1e9
+        ceil = atomic_ceiling(w)
+        roofline["atomics"] = {"adds_per_launch": adds, "achieved_G_per_s": round(rate, 1),
+                               "probe_ceiling_G_per_s": ceil,
+                               "frac": round(rate / ceil, 4) if ceil else None}
     value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     cpu = None

@@ -293,3 +293,15 @@ def test_traffic_classifies_kernel_names():
         ("dkdv", "full")
     assert classify("void fa::fwd_kernel<128, 64, 4, 2, false, true>(fa::FwdArgs)") is None   # dropout
     assert classify("void fa::preprocess_kernel<128>(fa::PreArgs)") == ("preprocess", None)
+
+
+def test_bench_atomic_add_count():
+    """Atomic adds of the fused dQ: N/BK per dq element without the mask; with the causal mask key
+    tile kt starts at query row kt*BK (BK a multiple of BQ), so it adds to N - kt*BK rows."""
+    import bench
+    B, H, N, d, bk, bq = 2, 3, 1024, 64, 256, 64
+    assert bench.atomic_adds_per_launch(B, H, N, d, False, bk, bq) == B * H * N * d * (N // bk)
+    rows = sum(N - kt * bk for kt in range(N // bk))
+    assert bench.atomic_adds_per_launch(B, H, N, d, True, bk, bq) == B * H * rows * d
+    # ragged: padded rows past N are not added
+    assert bench.atomic_adds_per_launch(1, 1, 100, 8, False, 64, 32) == 100 * 8 * 2
