@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dropout.restype = i
     L.fa_dropout_keep_scale.argtypes = [ctypes.c_double]
     L.fa_dropout_keep_scale.restype = ctypes.c_double
+    L.fa_fwd_general_dropout.argtypes = [vp, st, vp, st, vp, st, i, i, i, i, i, f, dr, vp, st, vp, vp, sz, vp]
+    L.fa_fwd_general_dropout.restype = i
+    L.fa_bwd_general_dropout.argtypes = [vp, st, vp, st, vp, st, vp, st, vp, vp, st, i, i, i, i, i, f, dr, i,
+                                         vp, st, vp, st, vp, st, vp, sz, vp]
+    L.fa_bwd_general_dropout.restype = i
     _lib = L
     return L
 
@@ -322,9 +327,20 @@ def _workspace(need, device, workspace):
     return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
 
 
-def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, workspace=None, stream=None):
+def _dropout_arg(dropout):
+    """(p, seed[, offset]) or FaDropout -> FaDropout."""
+    if isinstance(dropout, FaDropout):
+        return dropout
+    p, seed = dropout[0], dropout[1]
+    off = dropout[2] if len(dropout) > 2 else 0
+    return FaDropout(float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(off) & 0xFFFFFFFF)
+
+
+def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, workspace=None, stream=None,
+                   dropout=None):
     """Forward for any head dim 1..256 and strided [B, H, N, d] views (e.g. a [B, N, H, d] tensor
-    transposed); returns (o, lse).  o defaults to a new contiguous fp32 tensor."""
+    transposed); returns (o, lse).  o defaults to a new contiguous fp32 tensor.  dropout = (p, seed,
+    offset) runs fa_fwd_general_dropout."""
     torch = _torch()
     B, H, N, d = q.shape
     pq, sq = _view(q, "q", torch.bfloat16, q.shape)
@@ -337,17 +353,21 @@ def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, worksp
     po, so = _view(o, "o", torch.float32, q.shape)
     pl = _check(lse, "lse", torch.float32, (B, H, N))
     workspace, pw, wb = _workspace(fa_fwd_general_workspace_size(B, H, N, d), q.device, workspace)
-    st = lib().fa_fwd_general(pq, sq, pk, sk, pv, sv, B, H, N, d, int(bool(causal)), float(scale), po, so, pl, pw, wb,
-                              _stream_ptr(stream))
+    if dropout is None:
+        st = lib().fa_fwd_general(pq, sq, pk, sk, pv, sv, B, H, N, d, int(bool(causal)), float(scale), po, so, pl, pw,
+                                  wb, _stream_ptr(stream))
+    else:
+        st = lib().fa_fwd_general_dropout(pq, sq, pk, sk, pv, sv, B, H, N, d, int(bool(causal)), float(scale),
+                                          _dropout_arg(dropout), po, so, pl, pw, wb, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_general")
     return o, lse
 
 
 def fa_bwd_general(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
-                   dq=None, dk=None, dv=None, workspace=None, stream=None):
+                   dq=None, dk=None, dv=None, workspace=None, stream=None, dropout=None):
     """Backward for any head dim 1..256 and strided views; returns (dq, dk, dv) (new contiguous fp32
-    tensors unless given)."""
+    tensors unless given).  dropout = the forward's (p, seed, offset) runs fa_bwd_general_dropout."""
     torch = _torch()
     B, H, N, d = q.shape
     args = [_view(q, "q", torch.bfloat16, q.shape), _view(k, "k", torch.bfloat16, q.shape),
@@ -359,8 +379,13 @@ def fa_bwd_general(q, k, v, o, lse, dout, causal: bool, scale: float, variant: i
     pouts = [_view(t, n, torch.float32, q.shape) for t, n in zip(outs, ("dq", "dk", "dv"))]
     workspace, pw, wb = _workspace(fa_bwd_general_workspace_size(B, H, N, d, variant), q.device, workspace)
     flat = [x for pair in args for x in pair]
-    st = lib().fa_bwd_general(*flat, pl, pdo, sdo, B, H, N, d, int(bool(causal)), float(scale), int(variant),
-                              *[x for pair in pouts for x in pair], pw, wb, _stream_ptr(stream))
+    flat_outs = [x for pair in pouts for x in pair]
+    if dropout is None:
+        st = lib().fa_bwd_general(*flat, pl, pdo, sdo, B, H, N, d, int(bool(causal)), float(scale), int(variant),
+                                  *flat_outs, pw, wb, _stream_ptr(stream))
+    else:
+        st = lib().fa_bwd_general_dropout(*flat, pl, pdo, sdo, B, H, N, d, int(bool(causal)), float(scale),
+                                          _dropout_arg(dropout), int(variant), *flat_outs, pw, wb, _stream_ptr(stream))
     if st != FA_OK:
         raise FAError(st, "fa_bwd_general")
     return tuple(outs)

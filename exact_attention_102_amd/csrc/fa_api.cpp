@@ -522,9 +522,14 @@ size_t fa_bwd_general_workspace_size(int B, int H, int N, int d, fa_bwd_variant 
   return 4 * align256(el * 2) + 4 * align256(el * 4) + fa_bwd_workspace_size(B, H, N, dp, variant);
 }
 
-fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
-                         fa_strides v_str, int B, int H, int N, int d, int causal, float scale, float* o,
-                         fa_strides o_str, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+fa_status fwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                           fa_strides v_str, int B, int H, int N, int d, int causal, float scale, float* o,
+                           fa_strides o_str, float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                           const DropSpec* drop) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   const fa_status sz = check_general(B, H, N, d, scale);
   if (sz != FA_OK) return sz;
@@ -543,7 +548,7 @@ fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
   const bool direct = supported_d(d) && contiguous(q_str, H, N, d) && contiguous(k_str, H, N, d) &&
                       contiguous(v_str, H, N, d) && contiguous(o_str, H, N, d) && aligned16(q) && aligned16(k) &&
                       aligned16(v) && aligned16(o);
-  if (direct) return fa_fwd_ex(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1);
+  if (direct) return fwd_impl(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1, drop);
 
   const size_t need = fa_fwd_general_workspace_size(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -566,17 +571,44 @@ fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
   fa::launch_gather_bf16(v, view_of(v_str), vp, B, H, N, d, dp, s);
   fa_status st = launched();
   if (st != FA_OK) return st;
-  st = fa_fwd_ex(qp, kp, vp, B, H, N, dp, causal, scale, op, lse, stream, -1);
+  st = fwd_impl(qp, kp, vp, B, H, N, dp, causal, scale, op, lse, stream, -1, drop);
   if (st != FA_OK) return st;
   fa::launch_scatter_f32(op, o, view_of(o_str), B, H, N, d, dp, s);
   return launched();
 }
 
-fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
-                         fa_strides v_str, const float* o, fa_strides o_str, const float* lse, const void* dout,
-                         fa_strides dout_str, int B, int H, int N, int d, int causal, float scale,
-                         fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
-                         float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, int B, int H, int N, int d, int causal, float scale, float* o,
+                         fa_strides o_str, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_general_impl(q, q_str, k, k_str, v, v_str, B, H, N, d, causal, scale, o, o_str, lse, workspace,
+                          workspace_bytes, stream, nullptr);
+}
+
+fa_status fa_fwd_general_dropout(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                                 fa_strides v_str, int B, int H, int N, int d, int causal, float scale,
+                                 fa_dropout dropout, float* o, fa_strides o_str, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  DropSpec ds;
+  const fa_status st = drop_spec(dropout, &ds);
+  if (st != FA_OK) return st;
+  return fwd_general_impl(q, q_str, k, k_str, v, v_str, B, H, N, d, causal, scale, o, o_str, lse, workspace,
+                          workspace_bytes, stream, &ds);
+}
+
+}  // extern "C"
+
+namespace {
+
+fa_status bwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                           fa_strides v_str, const float* o, fa_strides o_str, const float* lse, const void* dout,
+                           fa_strides dout_str, int B, int H, int N, int d, int causal, float scale,
+                           fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
+                           float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream,
+                           const DropSpec* drop) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const fa_status sz = check_general(B, H, N, d, scale);
   if (sz != FA_OK) return sz;
@@ -605,8 +637,8 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
                       aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dout) &&
                       aligned16(dq) && aligned16(dk) && aligned16(dv);
   if (direct)
-    return fa_bwd_ex(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace,
-                     workspace_bytes, stream, -1, -1);
+    return bwd_impl(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace,
+                    workspace_bytes, stream, -1, -1, drop);
 
   const size_t need = fa_bwd_general_workspace_size(B, H, N, d, variant);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -638,13 +670,39 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
   fa::launch_gather_f32(o, view_of(o_str), op, B, H, N, d, dp, s);
   fa_status st = launched();
   if (st != FA_OK) return st;
-  st = fa_bwd_ex(qp, kp, vp, op, lse, dop, B, H, N, dp, causal, scale, variant, dqp, dkp, dvp, ws, inner, stream, -1,
-                 -1);
+  st = bwd_impl(qp, kp, vp, op, lse, dop, B, H, N, dp, causal, scale, variant, dqp, dkp, dvp, ws, inner, stream, -1,
+                -1, drop);
   if (st != FA_OK) return st;
   fa::launch_scatter_f32(dqp, dq, view_of(dq_str), B, H, N, d, dp, s);
   fa::launch_scatter_f32(dkp, dk, view_of(dk_str), B, H, N, d, dp, s);
   fa::launch_scatter_f32(dvp, dv, view_of(dv_str), B, H, N, d, dp, s);
   return launched();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                         fa_strides v_str, const float* o, fa_strides o_str, const float* lse, const void* dout,
+                         fa_strides dout_str, int B, int H, int N, int d, int causal, float scale,
+                         fa_bwd_variant variant, float* dq, fa_strides dq_str, float* dk, fa_strides dk_str,
+                         float* dv, fa_strides dv_str, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_general_impl(q, q_str, k, k_str, v, v_str, o, o_str, lse, dout, dout_str, B, H, N, d, causal, scale,
+                          variant, dq, dq_str, dk, dk_str, dv, dv_str, workspace, workspace_bytes, stream, nullptr);
+}
+
+fa_status fa_bwd_general_dropout(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                                 fa_strides v_str, const float* o, fa_strides o_str, const float* lse,
+                                 const void* dout, fa_strides dout_str, int B, int H, int N, int d, int causal,
+                                 float scale, fa_dropout dropout, fa_bwd_variant variant, float* dq,
+                                 fa_strides dq_str, float* dk, fa_strides dk_str, float* dv, fa_strides dv_str,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  DropSpec ds;
+  const fa_status st = drop_spec(dropout, &ds);
+  if (st != FA_OK) return st;
+  return bwd_general_impl(q, q_str, k, k_str, v, v_str, o, o_str, lse, dout, dout_str, B, H, N, d, causal, scale,
+                          variant, dq, dq_str, dk, dk_str, dv, dv_str, workspace, workspace_bytes, stream, &ds);
 }
 
 }  // extern "C"

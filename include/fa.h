@@ -195,7 +195,8 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
  * The forward computes o = (P * M * s) v with lse that of the undropped scores;
  * the backward gives the gradients of sum(dout * o) for that same mask, redrawn
  * from (seed, offset): pass the forward's values.  A p that rounds to t = 0 runs the
- * plain kernels.  Head dims 64, 128, 256; each pass runs one tile shape per head dim.
+ * plain kernels.  Head dims 64, 128, 256 here (any d in 1..256 through the general
+ * dropout entries below); each pass runs one tile shape per head dim.
  * Errors as above; p outside [0, 1) or not finite is FA_ERR_INVALID_ARG. */
 typedef struct {
   double p;                /* drop probability, 0 <= p < 1                           */
@@ -214,6 +215,20 @@ fa_status fa_bwd_dropout(const void* q, const void* k, const void* v, const floa
 /* The factor kept probabilities are scaled by for drop probability p: 65536 / (65536 - t);
  * -1 if p is outside [0, 1). */
 double fa_dropout_keep_scale(double p);
+/* Dropout through the general entry points (any d in 1..256, strided views): arguments,
+ * workspace and errors as fa_fwd_general / fa_bwd_general.  The keep decisions depend on
+ * (b, h, i, j) only, so they are the same as those of fa_fwd_dropout for the same seed,
+ * offset and sequence positions. */
+fa_status fa_fwd_general_dropout(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                                 fa_strides v_str, int B, int H, int N, int d, int causal, float scale,
+                                 fa_dropout dropout, float* o, fa_strides o_str, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+fa_status fa_bwd_general_dropout(const void* q, fa_strides q_str, const void* k, fa_strides k_str, const void* v,
+                                 fa_strides v_str, const float* o, fa_strides o_str, const float* lse,
+                                 const void* dout, fa_strides dout_str, int B, int H, int N, int d, int causal,
+                                 float scale, fa_dropout dropout, fa_bwd_variant variant, float* dq,
+                                 fa_strides dq_str, float* dk, fa_strides dk_str, float* dv, fa_strides dv_str,
+                                 void* workspace, size_t workspace_bytes, void* stream);
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(fa_status s);
 

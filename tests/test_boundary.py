@@ -280,6 +280,35 @@ def test_dropout_entries_validate_and_keep_scale(L):
     assert dbwd(ws=0) == FA_ERR_WORKSPACE
     assert dbwd(wsb=need - 16) == FA_ERR_WORKSPACE
 
+    # general (strided, any d) dropout entries validate the same way
+    from exact_attention_102_amd.binding import FaStrides
+    dg = 96
+    t = FaStrides(N * H * dg, dg, H * dg)
+    gneed = L.fa_fwd_general_workspace_size(B, H, N, dg)
+
+    def gfwd(p=0.1, d=dg, wsb=gneed):
+        return L.fa_fwd_general_dropout(ctypes.c_void_p(P), t, ctypes.c_void_p(P + 64 * MB), t,
+                                        ctypes.c_void_p(P + 128 * MB), t, B, H, N, d, 0, 0.1, FaDropout(p, 1, 0),
+                                        ctypes.c_void_p(P + 192 * MB), t, ctypes.c_void_p(P + 256 * MB),
+                                        ctypes.c_void_p(P + 512 * MB), wsb, None)
+
+    assert gfwd(p=1.0) == FA_ERR_INVALID_ARG
+    assert gfwd(d=300) == FA_ERR_UNSUPPORTED
+    assert gfwd(wsb=gneed - 1) == FA_ERR_WORKSPACE
+    bneed = L.fa_bwd_general_workspace_size(B, H, N, dg, 1)
+
+    def gbwd(p=0.1, wsb=bneed):
+        views = []
+        for i in range(4):
+            views += [ctypes.c_void_p(P + i * 64 * MB), t]
+        return L.fa_bwd_general_dropout(*views, ctypes.c_void_p(P + 320 * MB), ctypes.c_void_p(P + 384 * MB), t, B, H,
+                                        N, dg, 0, 0.1, FaDropout(p, 1, 0), 1, ctypes.c_void_p(P + 600 * MB), t,
+                                        ctypes.c_void_p(P + 700 * MB), t, ctypes.c_void_p(P + 800 * MB), t,
+                                        ctypes.c_void_p(P + 1024 * MB), wsb, None)
+
+    assert gbwd(p=-1.0) == FA_ERR_INVALID_ARG
+    assert gbwd(wsb=bneed - 16) == FA_ERR_WORKSPACE
+
 
 def test_traffic_classifies_kernel_names():
     """The counter summary keys kernels by pass and mask from their template arguments."""

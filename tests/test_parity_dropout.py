@@ -13,6 +13,9 @@ ABI) against the fp64 oracle (oracle/dropout.py).
   per-element bound the test applies; dK = scale dS^T Q = 0.
 * p = 0 (and any p below 2^-16) runs the plain kernels bit for bit; the mask is a
   function of (seed, offset) only: same values give identical results, others differ.
+* The general entry points with dropout: head dims 40, 96, 192 (zero-padded path) on
+  [B, N, H, d] views at the same bar, and bit-identity with the fixed entry at d = 64
+  both as a strided view and contiguous.
 """
 import math
 
@@ -182,3 +185,52 @@ def test_dropout_workload_size_sampled_heads(variant):
         check_forward(o_s, l_s, ro[None], rl[None])
         g = [t.reshape(B * H, N, d)[heads].unsqueeze(0) for t in grads[variant]]
         check_backward(g, [r[None] for r in refs])
+
+
+@pytest.mark.parametrize("d", [40, 96, 192])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_general_head_dims_and_views(d, causal):
+    """Any head dim through the padded path, inputs and outputs as [B, N, H, d] views; the keep
+    decisions depend on (b, h, i, j) only, so the oracle's mask applies unchanged."""
+    from exact_attention_102_amd import fa_bwd_general, fa_fwd_general
+    B, H, N = 2, 3, 150
+    scale = 1.0 / math.sqrt(d)
+    p, off = 0.3, 9
+    note("general dropout d=%d causal=%d" % (d, causal))
+    dev, host, _ = make_inputs(B, H, N, d, seed=600 + d)
+    views = [x.transpose(1, 2).contiguous().transpose(1, 2) for x in dev]
+
+    def bnhd():
+        return torch.empty((B, N, H, d), dtype=torch.float32, device="cuda").transpose(1, 2)
+
+    o, lse = fa_fwd_general(*views[:3], causal, scale, o=bnhd(), dropout=(p, SEED, off))
+    torch.cuda.synchronize()
+    q, k, v, do = host
+    ro, rl = oracle.attention_forward_dropout_batched(q, k, v, scale, causal, p, SEED, off)
+    check_forward(o.contiguous(), lse, ro, rl)
+    refs = oracle.attention_backward_dropout_batched(q, k, v, do, scale, causal, p, SEED, off)
+    for name, var in VARIANTS.items():
+        note("  bwd %s" % name)
+        g = fa_bwd_general(*views[:3], o, lse, views[3], causal, scale, var, dq=bnhd(), dk=bnhd(), dv=bnhd(),
+                           dropout=(p, SEED, off))
+        torch.cuda.synchronize()
+        check_backward([t.contiguous() for t in g], refs)
+
+
+def test_dropout_general_matches_fixed_entry():
+    """d = 64 as a strided view (padded path) and contiguous (direct path) give the fixed entry's bits."""
+    from exact_attention_102_amd import FA_BWD_7GEMM, fa_bwd_dropout, fa_bwd_general, fa_fwd_dropout, fa_fwd_general
+    B, H, N, d = 1, 2, 200, 64
+    scale = 0.125
+    dev, _, _ = make_inputs(B, H, N, d, seed=31)
+    q, k, v, do = dev
+    o1, l1 = fa_fwd_dropout(q, k, v, True, scale, 0.25, 123, 4)
+    g1 = fa_bwd_dropout(q, k, v, o1, l1, do, True, scale, 0.25, 123, 4, variant=FA_BWD_7GEMM)
+    for views in (dev, [x.transpose(1, 2).contiguous().transpose(1, 2) for x in dev]):
+        o2, l2 = fa_fwd_general(*views[:3], True, scale, dropout=(0.25, 123, 4))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        g2 = fa_bwd_general(*views[:3], o2, l2, views[3], True, scale, FA_BWD_7GEMM, dropout=(0.25, 123, 4))
+        torch.cuda.synchronize()
+        for a, b in zip(g1, g2):
+            assert torch.equal(a, b)
