@@ -121,6 +121,21 @@ fa_status drop_spec(const fa_dropout& d, DropSpec* out) {
   return FA_OK;
 }
 
+// Element views of one call's tensors and their head dim hd (<= the kernels' D).
+struct Views {
+  fa::View q, k, v, o, dout, dq, dk, dv;
+  int hd;
+};
+
+fa::View contiguous_view(int H, int N, int d) {
+  return fa::View{(long long)H * N * d, (long long)N * d, (long long)d};
+}
+
+Views contiguous_views(int H, int N, int d) {
+  const fa::View c = contiguous_view(H, N, d);
+  return Views{c, c, c, c, c, c, c, c, d};
+}
+
 template <class Args>
 void set_drop(Args& a, const DropSpec* d) {
   if (!d || d->t == 0) return;
@@ -187,6 +202,38 @@ int fa_default_config(int pass, int d, int causal) {
 
 namespace {
 
+// The forward's launch on validated views: kernels built for head dim D (64, 128, 256),
+// tensors with head dim vw.hd <= D.  With dropout (drop->t != 0) the dropout table's
+// shape for D runs and cfg is ignored.
+fa_status fwd_launch(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int D,
+                     int causal, float scale, void* stream, int cfg, const DropSpec* drop, const Views& vw) {
+  const bool dropping = drop && drop->t != 0;
+  int n = 0;
+  const FwdConfig* t = dropping ? fa::fwd_dropout_configs(&n) : fwd_table(&n);
+  const int idx = dropping ? 0 : (cfg < 0 ? default_index(0, D, causal) : cfg);
+  const int j = nth_for_d(t, n, D, idx);
+  if (j < 0) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdArgs a;
+  a.q = static_cast<const __bf16*>(q);
+  a.k = static_cast<const __bf16*>(k);
+  a.v = static_cast<const __bf16*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.scale = scale;
+  a.vq = vw.q;
+  a.vk = vw.k;
+  a.vv = vw.v;
+  a.vo = vw.o;
+  a.hd = vw.hd;
+  set_drop(a, drop);
+  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
 // fa_fwd_ex, optionally with dropout (drop->t != 0: the dropout table's shape for d; cfg ignored).
 fa_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, int N, int d, int causal, float scale,
                    float* o, float* lse, void* stream, int cfg, const DropSpec* drop) {
@@ -201,26 +248,7 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, int B, int H, in
     if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_INVALID_ARG;
   if (overlaps(ro, rl)) return FA_ERR_INVALID_ARG;
 
-  const bool dropping = drop && drop->t != 0;
-  int n = 0;
-  const FwdConfig* t = dropping ? fa::fwd_dropout_configs(&n) : fwd_table(&n);
-  const int idx = dropping ? 0 : (cfg < 0 ? default_index(0, d, causal) : cfg);
-  const int j = nth_for_d(t, n, d, idx);
-  if (j < 0) return FA_ERR_UNSUPPORTED;
-
-  fa::FwdArgs a;
-  a.q = static_cast<const __bf16*>(q);
-  a.k = static_cast<const __bf16*>(k);
-  a.v = static_cast<const __bf16*>(v);
-  a.o = o;
-  a.lse = lse;
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.scale = scale;
-  set_drop(a, drop);
-  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
-  return launched();
+  return fwd_launch(q, k, v, o, lse, B, H, N, d, causal, scale, stream, cfg, drop, contiguous_views(H, N, d));
 }
 
 }  // namespace
@@ -276,14 +304,21 @@ fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int 
   p.delta = delta;
   p.dq = zero_dq ? dq : nullptr;
   p.rows = B * H * N;
+  p.H = H;
+  p.N = N;
+  p.hd = d;
+  p.vo = p.vdo = p.vdq = contiguous_view(H, N, d);
   if (fa::launch_preprocess(p, d, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_UNSUPPORTED;
   return launched();
 }
 
+}  // extern "C"
+
 namespace {
 
 fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                     const float* delta, int B, int H, int N, float scale, float* dq, float* dk, float* dv) {
+                     const float* delta, int B, int H, int N, float scale, float* dq, float* dk, float* dv,
+                     const Views& vw) {
   fa::BwdArgs a;
   a.q = static_cast<const __bf16*>(q);
   a.k = static_cast<const __bf16*>(k);
@@ -298,6 +333,14 @@ fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* do
   a.H = H;
   a.N = N;
   a.scale = scale;
+  a.vq = vw.q;
+  a.vk = vw.k;
+  a.vv = vw.v;
+  a.vdo = vw.dout;
+  a.vdq = vw.dq;
+  a.vdk = vw.dk;
+  a.vdv = vw.dv;
+  a.hd = vw.hd;
   return a;
 }
 
@@ -330,6 +373,8 @@ fa_status check_bwd_stage(const void* q, const void* k, const void* v, const voi
 
 }  // namespace
 
+extern "C" {
+
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                       const float* delta, int B, int H, int N, int d, int causal, float scale, int atomic_dq,
                       float* dq, float* dk, float* dv, void* stream, int cfg) {
@@ -341,7 +386,8 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
   const BwdConfig* t = bwd_table(pass, &n);
   const int j = nth_for_d(t, n, d, cfg < 0 ? default_index(pass, d, causal) : cfg);
   if (j < 0) return FA_ERR_UNSUPPORTED;
-  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, atomic_dq ? dq : nullptr, dk, dv);
+  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, atomic_dq ? dq : nullptr, dk, dv,
+                                 contiguous_views(H, N, d));
   if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
   return launched();
 }
@@ -356,7 +402,8 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   const BwdConfig* t = bwd_table(3, &n);
   const int j = nth_for_d(t, n, d, cfg < 0 ? default_index(3, d, causal) : cfg);
   if (j < 0) return FA_ERR_UNSUPPORTED;
-  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, nullptr, nullptr);
+  const fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, nullptr, nullptr,
+                                 contiguous_views(H, N, d));
   if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
   return launched();
 }
@@ -364,6 +411,11 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
 }  // extern "C"
 
 namespace {
+
+fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                     int B, int H, int N, int D, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                     float* dv, float* delta, void* stream, int cfg_dkdv, int cfg_dq, const DropSpec* drop,
+                     const Views& vw);
 
 // fa_bwd_ex, optionally with dropout (the dropout tables' shape for d; cfg_* ignored).
 fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -393,6 +445,23 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, 
       if (overlaps(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
   }
 
+  return bwd_launch(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv,
+                    static_cast<float*>(workspace), stream, cfg_dkdv, cfg_dq, drop, contiguous_views(H, N, d));
+}
+
+}  // namespace
+
+namespace {
+
+// The backward's launches on validated views (kernels built for head dim D, tensors with
+// head dim vw.hd <= D): preprocess into delta (and dq cleared for the atomic variant),
+// dK/dV (with atomic dQ), then the dQ kernel for the 7-GEMM variant.
+fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
+                     int B, int H, int N, int D, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
+                     float* dv, float* delta, void* stream, int cfg_dkdv, int cfg_dq, const DropSpec* drop,
+                     const Views& vw) {
+  const int d = D;
+  const size_t rows = (size_t)B * H * N;
   const bool atomic = variant == FA_BWD_5GEMM_ATOMIC;
   const bool dropping = drop && drop->t != 0;
   int n1 = 0, n3 = 0;
@@ -409,18 +478,23 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, 
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* delta = static_cast<float*>(workspace);
   fa::PreArgs p;
   p.o = o;
   p.dout = static_cast<const __bf16*>(dout);
   p.delta = delta;
   p.dq = atomic ? dq : nullptr;
   p.rows = (int)rows;
+  p.H = H;
+  p.N = N;
+  p.hd = vw.hd;
+  p.vo = vw.o;
+  p.vdo = vw.dout;
+  p.vdq = vw.dq;
   if (fa::launch_preprocess(p, d, s) != 0) return FA_ERR_UNSUPPORTED;
   fa_status st = launched();
   if (st != FA_OK) return st;
 
-  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv);
+  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv, vw);
   set_drop(a, drop);
   if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   st = launched();
@@ -474,10 +548,6 @@ bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p
 
 fa::View view_of(fa_strides s) { return fa::View{s.b, s.h, s.n}; }
 
-bool contiguous(fa_strides s, int H, int N, int d) {
-  return s.n == d && s.h == (long long)N * d && s.b == (long long)H * N * d;
-}
-
 // Byte range spanned by a view (its bounding interval); -1 strides are rejected earlier.
 Range view_range(const void* p, fa_strides s, int B, int H, int N, int d, size_t elem) {
   const long long last = (long long)(B - 1) * s.b + (long long)(H - 1) * s.h + (long long)(N - 1) * s.n + (d - 1);
@@ -492,6 +562,15 @@ fa_status check_general(int B, int H, int N, int d, float scale) {
 }
 
 bool strides_ok(fa_strides s) { return s.b >= 0 && s.h >= 0 && s.n >= 0; }
+
+// A view the kernels can read or write in place: 16-byte aligned base and row starts
+// (strides in multiples of 16 bytes), and a head's rows within the 32-bit (< 2^31
+// bytes) range of one buffer resource.
+bool direct_view(const void* p, fa_strides s, int N, size_t elem) {
+  const long long q = 16 / (long long)elem;
+  return aligned16(p) && s.b % q == 0 && s.h % q == 0 && s.n % q == 0 &&
+         (long long)N * s.n * (long long)elem < (1LL << 31);
+}
 
 struct Carve {
   char* p;
@@ -545,10 +624,18 @@ fa_status fwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
     if (overlaps(r, ro) || overlaps(r, rl)) return FA_ERR_INVALID_ARG;
   if (overlaps(ro, rl)) return FA_ERR_INVALID_ARG;
 
-  const bool direct = supported_d(d) && contiguous(q_str, H, N, d) && contiguous(k_str, H, N, d) &&
-                      contiguous(v_str, H, N, d) && contiguous(o_str, H, N, d) && aligned16(q) && aligned16(k) &&
-                      aligned16(v) && aligned16(o);
-  if (direct) return fwd_impl(q, k, v, B, H, N, d, causal, scale, o, lse, stream, -1, drop);
+  // In place when d is a multiple of 8 and every row is 16-byte aligned: the kernels pad the
+  // head dim to the next built size themselves.  Otherwise: padded contiguous copies.
+  const bool direct = d % 8 == 0 && direct_view(q, q_str, N, 2) && direct_view(k, k_str, N, 2) &&
+                      direct_view(v, v_str, N, 2) && direct_view(o, o_str, N, 4);
+  if (direct) {
+    Views vw = contiguous_views(H, N, d);
+    vw.q = view_of(q_str);
+    vw.k = view_of(k_str);
+    vw.v = view_of(v_str);
+    vw.o = view_of(o_str);
+    return fwd_launch(q, k, v, o, lse, B, H, N, padded_d(d), causal, scale, stream, -1, drop, vw);
+  }
 
   const size_t need = fa_fwd_general_workspace_size(B, H, N, d);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -631,14 +718,32 @@ fa_status bwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
       if (overlaps(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
   }
 
-  const bool direct = supported_d(d) && contiguous(q_str, H, N, d) && contiguous(k_str, H, N, d) &&
-                      contiguous(v_str, H, N, d) && contiguous(o_str, H, N, d) && contiguous(dout_str, H, N, d) &&
-                      contiguous(dq_str, H, N, d) && contiguous(dk_str, H, N, d) && contiguous(dv_str, H, N, d) &&
-                      aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o) && aligned16(dout) &&
-                      aligned16(dq) && aligned16(dk) && aligned16(dv);
-  if (direct)
-    return bwd_impl(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, workspace,
-                    workspace_bytes, stream, -1, -1, drop);
+  const bool direct = d % 8 == 0 && direct_view(q, q_str, N, 2) && direct_view(k, k_str, N, 2) &&
+                      direct_view(v, v_str, N, 2) && direct_view(dout, dout_str, N, 2) &&
+                      direct_view(o, o_str, N, 4) && direct_view(dq, dq_str, N, 4) && direct_view(dk, dk_str, N, 4) &&
+                      direct_view(dv, dv_str, N, 4);
+  if (direct) {
+    const int dp = padded_d(d);
+    const size_t need = fa_bwd_workspace_size(B, H, N, dp, variant);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+    const Range rw = rng(workspace, need);
+    for (const Range& r : ins)
+      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+    for (const Range& r : outs)
+      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+    Views vw = contiguous_views(H, N, d);
+    vw.q = view_of(q_str);
+    vw.k = view_of(k_str);
+    vw.v = view_of(v_str);
+    vw.o = view_of(o_str);
+    vw.dout = view_of(dout_str);
+    vw.dq = view_of(dq_str);
+    vw.dk = view_of(dk_str);
+    vw.dv = view_of(dv_str);
+    return bwd_launch(q, k, v, o, lse, dout, B, H, N, dp, causal, scale, variant, dq, dk, dv,
+                      static_cast<float*>(workspace), stream, -1, -1, drop, vw);
+  }
 
   const size_t need = fa_bwd_general_workspace_size(B, H, N, d, variant);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;

@@ -27,7 +27,8 @@ __device__ __forceinline__ float bf16_bits_to_f32(unsigned short h) {
 
 // ---------------------------------------------------------------------------
 // delta_i = sum_k dO_ik * O_ik; optionally zero dq.  D / 8 threads per row, each
-// reading one 16-byte chunk of dO and two of O, then a shuffle reduction.
+// reading one 16-byte chunk of dO and two of O (chunks past the head dim hd add
+// nothing and are not cleared), then a shuffle reduction.
 template <int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   constexpr int TPR = D / 8;
@@ -36,11 +37,12 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
   const int row = blockIdx.x * RPB + tid / TPR;
   const int c = tid % TPR;
   float acc = 0.f;
-  if (row < a.rows) {
-    const size_t base = (size_t)row * D + c * 8;
-    const u32x4 dv = *(const u32x4*)(a.dout + base);
-    const f32x4 o0 = *(const f32x4*)(a.o + base);
-    const f32x4 o1 = *(const f32x4*)(a.o + base + 4);
+  if (row < a.rows && c * 8 < a.hd) {
+    const int bh = row / a.N, n = row % a.N;
+    const size_t obase = head_base(a.vo, bh, a.H) + (size_t)n * a.vo.sn + c * 8;
+    const u32x4 dv = *(const u32x4*)(a.dout + head_base(a.vdo, bh, a.H) + (size_t)n * a.vdo.sn + c * 8);
+    const f32x4 o0 = *(const f32x4*)(a.o + obase);
+    const f32x4 o1 = *(const f32x4*)(a.o + obase + 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const unsigned w = dv[e];
@@ -53,8 +55,9 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
     }
     if (a.dq) {
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *(f32x4*)(a.dq + base) = z;
-      *(f32x4*)(a.dq + base + 4) = z;
+      float* dqp = a.dq + head_base(a.vdq, bh, a.H) + (size_t)n * a.vdq.sn + c * 8;
+      *(f32x4*)dqp = z;
+      *(f32x4*)(dqp + 4) = z;
     }
   }
 #pragma unroll
@@ -268,7 +271,8 @@ struct DkdvMath {
   // tile late lets the atomics drain under the next tile's products instead of
   // holding up the end-of-tile wait.
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
-                                                   int N, float scale, int wave, int g, int l32, int lane) {
+                                                   int N, float scale, int wave, int g, int l32, int lane,
+                                                   long long dq_ld, int hd) {
     {
       for (int t = wave; t < QBN * DB; t += NW) {
         const int qb = t / DB, db = t % DB;
@@ -278,10 +282,20 @@ struct DkdvMath {
           acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
                        ColOffsets<D, KMODE>::col_dyn(ktile, ks * 16, db, lane), acc);
         }
+        // in-head element offsets fit 32 bits (N * row pitch < 2^31 is validated): one lane
+        // offset plus a wave-uniform offset per accumulator row.  Both are opaque to the
+        // optimiser, which would otherwise hoist all sixteen row offsets of every
+        // (query block, d block) pair out of the tile loop and hold them in registers.
+        int ld = (int)dq_ld;
+        asm volatile("" : "+s"(ld));
+        const int qlane = q0 + qb * 32 + 4 * g;
+        int lane_off = qlane * ld + db * 32 + l32;
+        asm volatile("" : "+v"(lane_off));
+        const bool col_ok = db * 32 + l32 < hd;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
+          const int ro = 8 * (r >> 2) + (r & 3);
+          if (qlane + ro < N && col_ok) unsafeAtomicAdd(dqh + (unsigned)(lane_off + ro * ld), acc[r] * scale);
         }
       }
     }
@@ -333,14 +347,15 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     bh = item / nkt;
     kt = item % nkt;
   }
-  const size_t head = (size_t)bh * N * D;
-  const __bf16* Qh = a.q + head;
-  const __bf16* Kh = a.k + head;
-  const __bf16* Vh = a.v + head;
-  const __bf16* dOh = a.dout + head;
+  const __bf16* Qh = a.q + head_base(a.vq, bh, a.H);
+  const __bf16* Kh = a.k + head_base(a.vk, bh, a.H);
+  const __bf16* Vh = a.v + head_base(a.vv, bh, a.H);
+  const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
   const float* lseh = a.lse + (size_t)bh * N;
   const float* delh = a.delta + (size_t)bh * N;
-  float* dqh = ATOMIC ? a.dq + head : nullptr;
+  float* dqh = ATOMIC ? a.dq + head_base(a.vdq, bh, a.H) : nullptr;
+  const int hd = a.hd;  // columns hd .. D-1 are zero padding
+  const long long dq_ld = a.vdq.sn;
   const float c = a.scale * kLog2e;
   const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
   const float ks = a.drop_scale;
@@ -351,18 +366,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
   constexpr int KMODE = M::KMODE;
-  TileDMA<BQ, D, NW, kBoth> qdma;  // Q, dO: row fragments and transposed reads
-  qdma.init(wave, lane);
+  TileDMA<BQ, D, NW, kBoth> qdma, ddma;  // Q, dO: row fragments and transposed reads
+  qdma.init(wave, lane, a.vq.sn, hd);
+  ddma.init(wave, lane, a.vdo.sn, hd);
   qdma.issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
-  qdma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
+  ddma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
   if constexpr (ATOMIC || KV_LDS) {
     TileDMA<BK, D, NW, KMODE> kd;
-    kd.init(wave, lane);
+    kd.init(wave, lane, a.vk.sn, hd);
     kd.issue(Kh, k0, N, ktile, wave, lane);
   }
   if constexpr (KV_LDS) {
     TileDMA<BK, D, NW, kRowOnly> vd;
-    vd.init(wave, lane);
+    vd.init(wave, lane, a.vv.sn, hd);
     vd.issue(Vh, k0, N, vtile, wave, lane);
   }
   RowStager<BQ, NT> srow;
@@ -374,8 +390,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     const int krow_g = min(key, N - 1);  // keys past the end are masked (P = 0) and never stored
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      kf[kk] = *(const bf16x8*)(Kh + (size_t)krow_g * D + kk * 16 + g * 8);
-      vf[kk] = *(const bf16x8*)(Vh + (size_t)krow_g * D + kk * 16 + g * 8);
+      kf[kk] = load_row_chunk(Kh + (size_t)krow_g * a.vk.sn, 2 * kk + g, hd >> 3);
+      vf[kk] = load_row_chunk(Vh + (size_t)krow_g * a.vv.sn, 2 * kk + g, hd >> 3);
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -405,19 +421,20 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pv.refresh();
     }
     qdma.refresh();
+    ddma.refresh();
     if (it + 1 < nqt) {
       qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
-      qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
+      ddma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
       srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
     if constexpr (ATOMIC && DEFER) {
-      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
+      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
     }
     M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst0, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
             pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
-      M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
+      M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
     }
     wait_tile();
     if (it + 1 < nqt) srow.store(st1, N, tid);
@@ -430,17 +447,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pv.refresh();
     }
     qdma.refresh();
+    ddma.refresh();
     if (it + 2 < nqt) {
       qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
-      qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
+      ddma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
       srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
-    if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
+    if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, DEFER ? dst1 : dst0, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N,
             c, a.scale, fr, fc, pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
-      M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane);
+      M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
     }
     wait_tile();
     if (it + 2 < nqt) srow.store(st0, N, tid);
@@ -448,12 +466,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   }
   if constexpr (ATOMIC && DEFER) {  // dQ of the last query tile (its dS^T buffer alternates with the tile's parity)
     const int last = nqt - 1;
-    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane);
+    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane, dq_ld,
+                 hd);
   }
 
   if (key < N) {
-    float* dkr = a.dk + head + (size_t)key * D;
-    float* dvr = a.dv + head + (size_t)key * D;
+    float* dkr = a.dk + head_base(a.vdk, bh, a.H) + (size_t)key * a.vdk.sn;
+    float* dvr = a.dv + head_base(a.vdv, bh, a.H) + (size_t)key * a.vdv.sn;
     const float vs = DROP ? ks : 1.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -464,8 +483,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
                           dk[db][4 * a4 + 3] * a.scale};
         const f32x4 vv = {dv[db][4 * a4] * vs, dv[db][4 * a4 + 1] * vs, dv[db][4 * a4 + 2] * vs,
                           dv[db][4 * a4 + 3] * vs};
-        *(f32x4*)(dkr + col) = kv;
-        *(f32x4*)(dvr + col) = vv;
+        if (col < hd) {
+          *(f32x4*)(dkr + col) = kv;
+          *(f32x4*)(dvr + col) = vv;
+        }
       }
     }
   }
@@ -559,11 +580,11 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     bh = item / nqt;
     qt = item % nqt;
   }
-  const size_t head = (size_t)bh * N * D;
-  const __bf16* Qh = a.q + head;
-  const __bf16* Kh = a.k + head;
-  const __bf16* Vh = a.v + head;
-  const __bf16* dOh = a.dout + head;
+  const __bf16* Qh = a.q + head_base(a.vq, bh, a.H);
+  const __bf16* Kh = a.k + head_base(a.vk, bh, a.H);
+  const __bf16* Vh = a.v + head_base(a.vv, bh, a.H);
+  const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
+  const int hd = a.hd;  // columns hd .. D-1 are zero padding
   const float c = a.scale * kLog2e;
   const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
 
@@ -575,8 +596,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   const int nkt = (kv_end + BC - 1) / BC;
   TileDMA<BC, D, NW, kBoth> kdma;     // K: row fragments and transposed reads
   TileDMA<BC, D, NW, kRowOnly> vdma;  // V: row fragments only
-  kdma.init(wave, lane);
-  vdma.init(wave, lane);
+  kdma.init(wave, lane, a.vk.sn, hd);
+  vdma.init(wave, lane, a.vv.sn, hd);
   kdma.issue(Kh, 0, N, kbuf0, wave, lane);
   vdma.issue(Vh, 0, N, vbuf0, wave, lane);
 
@@ -584,8 +605,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   bf16x8 qf[KK], dof[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    qf[kk] = *(const bf16x8*)(Qh + (size_t)qrow * D + kk * 16 + g * 8);
-    dof[kk] = *(const bf16x8*)(dOh + (size_t)qrow * D + kk * 16 + g * 8);
+    qf[kk] = load_row_chunk(Qh + (size_t)qrow * a.vq.sn, 2 * kk + g, hd >> 3);
+    dof[kk] = load_row_chunk(dOh + (size_t)qrow * a.vdo.sn, 2 * kk + g, hd >> 3);
   }
   const float lse2 = qi < N ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
   const float dl = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
@@ -633,14 +654,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   }
 
   if (qi < N) {
-    float* dqr = a.dq + head + (size_t)qi * D;
+    float* dqr = a.dq + head_base(a.vdq, bh, a.H) + (size_t)qi * a.vdq.sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
+        const int col = db * 32 + 8 * a4 + 4 * g;
         const f32x4 val = {dq[db][4 * a4] * a.scale, dq[db][4 * a4 + 1] * a.scale, dq[db][4 * a4 + 2] * a.scale,
                            dq[db][4 * a4 + 3] * a.scale};
-        *(f32x4*)(dqr + db * 32 + 8 * a4 + 4 * g) = val;
+        if (col < hd) *(f32x4*)(dqr + col) = val;
       }
     }
   }

@@ -206,30 +206,42 @@ __device__ __forceinline__ unsigned lds_addr(const LDS void* p) {
 // Direct-to-LDS copy of a ROWS x W bf16 tile: each wave instruction moves 64 x 16
 // bytes straight into 1 KB of contiguous LDS (lane l lands at base + 16 l),
 // bypassing registers.  Lane l therefore fetches the global chunk that belongs at
-// its LDS position under the swizzle.  The per-lane byte offsets of the pieces are
-// computed once (init) and kept opaque to the optimiser (refresh); each issue is
-// then one VALU-free instruction with a wave-uniform (SGPR) row offset.  Tiles
-// reaching past valid_rows take a slower path that clamps rows to the last valid
-// one: the kernels mask such keys (-inf scores) and give such queries P = 0, so the
-// duplicates never count.  The copy is asynchronous: wait_tile() (vmcnt) plus a
-// barrier must precede reads.
+// its LDS position under the swizzle.  Global rows are ld bytes apart (any
+// multiple of 16) and only their first nvalid 16-byte chunks exist: lanes whose
+// chunk lies beyond get an offset past the buffer's range, which the hardware's
+// range check turns into zeros without a memory access (the zero padding of a head
+// dim below W).  The per-lane byte offsets of the pieces are computed once (init)
+// and kept opaque to the optimiser (refresh); each issue is then one VALU-free
+// instruction with a wave-uniform (SGPR) row offset.  Tiles reaching past
+// valid_rows take a slower path that clamps rows to the last valid one: the kernels
+// mask such keys (-inf scores) and give such queries P = 0, so the duplicates never
+// count.  The copy is asynchronous: wait_tile() (vmcnt) plus a barrier must precede
+// reads.
+constexpr unsigned kOutOfRange = 0x80000000u;  // above every buffer range used here (< 2^31 bytes)
+
 template <int ROWS, int W, int NW, int MODE>
 struct TileDMA {
   static constexpr int kPieces = ROWS * W * 2 / 1024;
   static constexpr int kPerWave = kPieces / NW;
   static_assert(kPieces % NW == 0, "tile must split into whole 1 KB pieces per wave");
   unsigned off[kPerWave];
+  unsigned ld;      // global row pitch, bytes
+  int nvalid;       // 16-byte chunks per global row
 
   __device__ __forceinline__ static int piece_row(int piece, int lane) { return (piece * 1024 + lane * 16) / (2 * W); }
   __device__ __forceinline__ static int piece_chunk(int piece, int lane) {
     const int byte = piece * 1024 + lane * 16;
     return ((byte % (2 * W)) >> 4) ^ swz<W, MODE>(byte / (2 * W));
   }
-  __device__ __forceinline__ void init(int wave, int lane) {
+  // row_pitch_elems: the view's row stride (elements); head_dim: its valid columns
+  __device__ __forceinline__ void init(int wave, int lane, long long row_pitch_elems, int head_dim) {
+    ld = (unsigned)row_pitch_elems * 2u;
+    nvalid = head_dim >> 3;
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int piece = i * NW + wave;
-      off[i] = (unsigned)(piece_row(piece, lane) * (2 * W) + piece_chunk(piece, lane) * 16);
+      const int ch = piece_chunk(piece, lane);
+      off[i] = ch < nvalid ? (unsigned)piece_row(piece, lane) * ld + (unsigned)ch * 16u : kOutOfRange;
     }
   }
   __device__ __forceinline__ void refresh() {
@@ -237,13 +249,13 @@ struct TileDMA {
     for (int i = 0; i < kPerWave; ++i) asm volatile("" : "+v"(off[i]));
   }
   // wave must be wave-uniform (e.g. readfirstlane of threadIdx.x / 64); g is the
-  // head's base and valid_rows its row count (valid_rows * 2W < 2^32 bytes, so
-  // every offset fits the 32-bit buffer range, which also bounds the reads).
+  // head's base and valid_rows its row count (valid_rows * ld < 2^31 bytes, so every
+  // offset fits the 32-bit buffer range, which also bounds the reads).
   __device__ __forceinline__ void issue(const __bf16* g, int row0, int valid_rows, LDS char* tile, int wave,
                                         int lane) const {
-    const u32x4 rs = buffer_rsrc(g, (unsigned)valid_rows * (2u * W));
+    const u32x4 rs = buffer_rsrc(g, (unsigned)valid_rows * ld);
     if (row0 + ROWS <= valid_rows) {
-      const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)row0 * (2u * W));
+      const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)row0 * ld);
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) lds_dma16(rs, off[i], soff, lds_addr(tile + (i * NW + wave) * 1024));
     } else {
@@ -251,12 +263,22 @@ struct TileDMA {
       for (int i = 0; i < kPerWave; ++i) {
         const int piece = i * NW + wave;
         const int grow = min(row0 + piece_row(piece, lane), valid_rows - 1);
-        lds_dma16(rs, (unsigned)grow * (2u * W) + (unsigned)piece_chunk(piece, lane) * 16u, 0u,
+        const int ch = piece_chunk(piece, lane);
+        lds_dma16(rs, ch < nvalid ? (unsigned)grow * ld + (unsigned)ch * 16u : kOutOfRange, 0u,
                   lds_addr(tile + piece * 1024));
       }
     }
   }
 };
+
+// 16-byte register load of chunk `chunk` of a row (zeros past the head dim).
+__device__ __forceinline__ bf16x8 load_row_chunk(const __bf16* row, int chunk, int nvalid) {
+  if (chunk < nvalid) return *(const bf16x8*)(row + chunk * 8);
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+  return z;
+}
 
 // vmcnt(0) through the builtin (not inline assembly), so the compiler's own
 // wait-count tracking also learns that all of its vector-memory loads are done.

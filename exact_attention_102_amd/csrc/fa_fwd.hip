@@ -173,10 +173,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
     bh = item / nqt;
     qt = item % nqt;
   }
-  const size_t head = (size_t)bh * N * D;
-  const __bf16* Qh = a.q + head;
-  const __bf16* Kh = a.k + head;
-  const __bf16* Vh = a.v + head;
+  const __bf16* Qh = a.q + head_base(a.vq, bh, a.H);
+  const __bf16* Kh = a.k + head_base(a.vk, bh, a.H);
+  const __bf16* Vh = a.v + head_base(a.vv, bh, a.H);
+  const int hd = a.hd;  // columns hd .. D-1 are zero padding
   const float c = a.scale * kLog2e;
   const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
 
@@ -188,15 +188,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const int nkt = (kv_end + BC - 1) / BC;
   TileDMA<BC, D, NW, kRowOnly> kdma;  // K: row fragments only
   TileDMA<BC, D, NW, kColOnly> vdma;  // V: transposed fragments only
-  kdma.init(wave, lane);
-  vdma.init(wave, lane);
+  kdma.init(wave, lane, a.vk.sn, hd);
+  vdma.init(wave, lane, a.vv.sn, hd);
   kdma.issue(Kh, 0, N, kbuf0, wave, lane);
   vdma.issue(Vh, 0, N, vbuf0, wave, lane);
 
   bf16x8 qf[KK];
   const int qrow = min(qi, N - 1);  // rows past the end duplicate the last row; never stored
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) qf[kk] = *(const bf16x8*)(Qh + (size_t)qrow * D + kk * 16 + g * 8);
+  for (int kk = 0; kk < KK; ++kk) qf[kk] = load_row_chunk(Qh + (size_t)qrow * a.vq.sn, 2 * kk + g, hd >> 3);
 
   float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
   f32x16 o[DB];
@@ -240,14 +240,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   const float lt = half_swap_sum(l_run);
   const float inv = (DROP ? a.drop_scale : 1.f) / half_swap_sum(lb_run);
   if (qi < N) {
-    float* orow = a.o + head + (size_t)qi * D;
+    float* orow = a.o + head_base(a.vo, bh, a.H) + (size_t)qi * a.vo.sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
+        const int col = db * 32 + 8 * a4 + 4 * g;
         const f32x4 val = {o[db][4 * a4] * inv, o[db][4 * a4 + 1] * inv, o[db][4 * a4 + 2] * inv,
                            o[db][4 * a4 + 3] * inv};
-        *(f32x4*)(orow + db * 32 + 8 * a4 + 4 * g) = val;
+        if (col < hd) *(f32x4*)(orow + col) = val;
       }
     }
     if (g == 0) a.lse[(size_t)bh * N + qi] = (m_run + log2f(lt)) * kLn2;

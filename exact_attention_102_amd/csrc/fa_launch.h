@@ -5,6 +5,21 @@
 
 namespace fa {
 
+// Element strides of a [B, H, N, *] tensor (the head dim is contiguous): element
+// (b, h, n, i) is at base[b * sb + h * sh + n * sn + i].
+struct View {
+  long long sb, sh, sn;
+};
+
+// Every tensor is passed as a base pointer plus a View; hd is the tensors' head
+// dim.  The kernels are built for D = 64, 128, 256 >= hd: columns hd .. D-1 read as
+// zeros (the tile copies and register loads fetch nothing there) and are never
+// written, so the result is the attention of the hd columns (zero columns change
+// no score).  Row starts are 16-byte aligned and hd is a multiple of 8.
+__device__ __forceinline__ size_t head_base(const View& v, int bh, int H) {
+  return (size_t)(bh / H) * (size_t)v.sb + (size_t)(bh % H) * (size_t)v.sh;
+}
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
@@ -16,6 +31,8 @@ struct FwdArgs {
   // dropout on P (fa_dropout.h); drop_t == 0 means none
   unsigned drop_k0 = 0, drop_k1 = 0, drop_offset = 0, drop_t = 0;
   float drop_scale = 1.f;
+  View vq{}, vk{}, vv{}, vo{};
+  int hd = 0;
 };
 
 struct BwdArgs {
@@ -32,6 +49,8 @@ struct BwdArgs {
   float scale;
   unsigned drop_k0 = 0, drop_k1 = 0, drop_offset = 0, drop_t = 0;
   float drop_scale = 1.f;
+  View vq{}, vk{}, vv{}, vdo{}, vdq{}, vdk{}, vdv{};
+  int hd = 0;
 };
 
 struct PreArgs {
@@ -40,6 +59,8 @@ struct PreArgs {
   float* delta;
   float* dq;  // zeroed when non-null
   int rows;   // B * H * N
+  int H = 0, N = 0, hd = 0;
+  View vo{}, vdo{}, vdq{};
 };
 
 typedef int (*FwdLaunch)(const FwdArgs&, bool causal, hipStream_t);
@@ -75,11 +96,6 @@ const BwdConfig* dq_dropout_configs(int* count);
 
 int launch_preprocess(const PreArgs& a, int d, hipStream_t stream);
 
-// Element strides of a [B, H, N, d] view (the head dim is contiguous): element
-// (b, h, n, i) is at base[b * sb + h * sh + n * sn + i].
-struct View {
-  long long sb, sh, sn;
-};
 // General-entry layout adapters (fa_pad.hip): strided [B,H,N,d] view <-> contiguous
 // [B,H,N,dp] buffer; gathers zero-fill columns d .. dp-1.
 void launch_gather_bf16(const void* src, View s, void* dst, int B, int H, int N, int d, int dp, hipStream_t st);

@@ -203,7 +203,9 @@ def test_general_entries_validate_before_launching(L):
     assert L.fa_fwd_general_workspace_size(B, H, N, 257) == 0
     assert L.fa_bwd_general_workspace_size(B, H, N, 96, 5) == 0
 
-    d = 96
+    # d = 100 is not a multiple of 8, so these calls take the padded-copy path, the one that
+    # needs the workspace; every case below fails validation before anything is launched
+    d = 100
     c = FaStrides(H * N * d, N * d, d)            # contiguous
     t = FaStrides(N * H * d, d, H * d)            # a [B, N, H, d] tensor seen as [B, H, N, d]
     ws_need = L.fa_fwd_general_workspace_size(B, H, N, d)
@@ -239,6 +241,18 @@ def test_general_entries_validate_before_launching(L):
     assert gbwd(ws=0) == FA_ERR_WORKSPACE
     assert gbwd(wsb=bneed - 16) == FA_ERR_WORKSPACE
     assert gbwd(dq=P + 700 * MB) == FA_ERR_INVALID_ARG         # dq overlaps dk
+    assert gbwd(dq=P + 64 * MB) == FA_ERR_INVALID_ARG          # dq overlaps k
+
+    # d = 96 with 16-byte aligned rows runs in place (the kernels pad the head dim): the backward
+    # then needs only the row-term workspace of the padded size, checked before any launch
+    d = 96
+    t = FaStrides(N * H * d, d, H * d)
+    c = FaStrides(H * N * d, N * d, d)
+    inplace_need = L.fa_bwd_workspace_size(B, H, N, 128, 1)
+    assert 0 < inplace_need < L.fa_bwd_general_workspace_size(B, H, N, d, 1)
+    assert gbwd(ws=0) == FA_ERR_WORKSPACE
+    assert gbwd(wsb=inplace_need - 16) == FA_ERR_WORKSPACE
+    assert gbwd(ws=P + 700 * MB + 256) == FA_ERR_INVALID_ARG   # workspace overlaps dk
     assert gbwd(dq=P + 64 * MB) == FA_ERR_INVALID_ARG          # dq overlaps k
 
 
@@ -280,9 +294,10 @@ def test_dropout_entries_validate_and_keep_scale(L):
     assert dbwd(ws=0) == FA_ERR_WORKSPACE
     assert dbwd(wsb=need - 16) == FA_ERR_WORKSPACE
 
-    # general (strided, any d) dropout entries validate the same way
+    # general (strided, any d) dropout entries validate the same way (d = 100: the padded-copy path,
+    # so the workspace checks apply and nothing is launched)
     from exact_attention_102_amd.binding import FaStrides
-    dg = 96
+    dg = 100
     t = FaStrides(N * H * dg, dg, H * dg)
     gneed = L.fa_fwd_general_workspace_size(B, H, N, dg)
 

@@ -98,3 +98,44 @@ def test_general_native_contiguous_matches_fixed_entry():
     g1 = fa_bwd(*dev[:3], o1, l1, dev[3], True, scale, FA_BWD_7GEMM)
     for a, b in zip(g1, grads["7gemm"]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("d,pitch", [(96, 128), (40, 64), (64, 72), (64, 68)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_general_rows_wider_than_head_dim(d, pitch, causal):
+    """Views of the first d columns of [B, H, N, pitch] buffers whose other columns hold NaN.
+    Aligned pitches (128, 64, 72 elements) run in place, the kernels padding the head dim
+    themselves; pitch 68 (136-byte rows) takes the padded-copy path.  Nothing past column d may be
+    read (a NaN would spread into every result) or written (the NaNs must survive)."""
+    from exact_attention_102_amd import fa_bwd_general, fa_fwd_general
+    B, H, N = 2, 2, 130
+    scale = 1.0 / math.sqrt(d)
+    note("wide rows d=%d pitch=%d causal=%d" % (d, pitch, causal))
+    dev, host, _ = make_inputs(B, H, N, d, seed=900 + d + pitch)
+
+    def wide(x, dtype):
+        buf = torch.full((B, H, N, pitch), float("nan"), dtype=dtype, device="cuda")
+        if x is not None:
+            buf[..., :d] = x
+        return buf
+
+    bufs = [wide(x, torch.bfloat16) for x in dev]
+    views = [b[..., :d] for b in bufs]
+    obuf = wide(None, torch.float32)
+    o, lse = fa_fwd_general(*views[:3], causal, scale, o=obuf[..., :d])
+    torch.cuda.synchronize()
+    assert torch.isnan(obuf[..., d:]).all()
+    check_forward(o.contiguous(), lse, *oracle_forward(host, scale, causal))
+    refs = oracle_backward(host, scale, causal)
+    for name, var in VARIANTS.items():
+        note("  bwd %s" % name)
+        gbufs = [wide(None, torch.float32) for _ in range(3)]
+        if var == VARIANTS["5gemm"]:
+            for gb in gbufs:               # the atomic dq accumulates into what the library clears
+                gb[..., :d] = 123.0
+        g = fa_bwd_general(*views[:3], o, lse, views[3], causal, scale, var, dq=gbufs[0][..., :d],
+                           dk=gbufs[1][..., :d], dv=gbufs[2][..., :d])
+        torch.cuda.synchronize()
+        for gb in gbufs:
+            assert torch.isnan(gb[..., d:]).all()
+        check_backward([t.contiguous() for t in g], refs)
