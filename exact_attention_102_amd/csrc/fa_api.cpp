@@ -131,6 +131,8 @@ fa::View contiguous_view(int H, int N, int d) {
   return fa::View{(long long)H * N * d, (long long)N * d, (long long)d};
 }
 
+bool same_view(const fa::View& a, const fa::View& b) { return a.sb == b.sb && a.sh == b.sh && a.sn == b.sn; }
+
 Views contiguous_views(int H, int N, int d) {
   const fa::View c = contiguous_view(H, N, d);
   return Views{c, c, c, c, c, c, c, c, d};
@@ -414,8 +416,15 @@ namespace {
 
 fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                      int B, int H, int N, int D, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
-                     float* dv, float* delta, void* stream, int cfg_dkdv, int cfg_dq, const DropSpec* drop,
-                     const Views& vw);
+                     float* dv, float* delta, float* dq_scratch, void* stream, int cfg_dkdv, int cfg_dq,
+                     const DropSpec* drop, const Views& vw);
+
+// The 5-GEMM kernel accumulates dq in a contiguous [B, H, N, D] buffer: the caller's dq when
+// it has exactly that layout, otherwise a scratch buffer whose first hd columns are then
+// copied into the caller's view.
+bool atomic_dq_in_place(const Views& vw, int H, int N, int D) {
+  return vw.hd == D && same_view(vw.dq, contiguous_view(H, N, D));
+}
 
 // fa_bwd_ex, optionally with dropout (the dropout tables' shape for d; cfg_* ignored).
 fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
@@ -446,7 +455,7 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, 
   }
 
   return bwd_launch(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv,
-                    static_cast<float*>(workspace), stream, cfg_dkdv, cfg_dq, drop, contiguous_views(H, N, d));
+                    static_cast<float*>(workspace), nullptr, stream, cfg_dkdv, cfg_dq, drop, contiguous_views(H, N, d));
 }
 
 }  // namespace
@@ -458,9 +467,17 @@ namespace {
 // dK/dV (with atomic dQ), then the dQ kernel for the 7-GEMM variant.
 fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                      int B, int H, int N, int D, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
-                     float* dv, float* delta, void* stream, int cfg_dkdv, int cfg_dq, const DropSpec* drop,
-                     const Views& vw) {
+                     float* dv, float* delta, float* dq_scratch, void* stream, int cfg_dkdv, int cfg_dq,
+                     const DropSpec* drop, const Views& vw_in) {
   const int d = D;
+  Views vw = vw_in;
+  float* const dq_user = dq;
+  const bool dq_copy = variant == FA_BWD_5GEMM_ATOMIC && !atomic_dq_in_place(vw_in, H, N, D);
+  if (dq_copy) {
+    if (!dq_scratch) return FA_ERR_WORKSPACE;
+    dq = dq_scratch;
+    vw.dq = contiguous_view(H, N, D);
+  }
   const size_t rows = (size_t)B * H * N;
   const bool atomic = variant == FA_BWD_5GEMM_ATOMIC;
   const bool dropping = drop && drop->t != 0;
@@ -498,7 +515,12 @@ fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o
   set_drop(a, drop);
   if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   st = launched();
-  if (st != FA_OK || atomic) return st;
+  if (st != FA_OK) return st;
+  if (atomic) {
+    if (!dq_copy) return FA_OK;
+    fa::launch_scatter_f32(dq_scratch, dq_user, vw_in.dq, B, H, N, vw_in.hd, D, s);
+    return launched();
+  }
   if (t3[i3].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   return launched();
 }
@@ -718,20 +740,12 @@ fa_status bwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
       if (overlaps(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
   }
 
-  const bool direct = d % 8 == 0 && direct_view(q, q_str, N, 2) && direct_view(k, k_str, N, 2) &&
-                      direct_view(v, v_str, N, 2) && direct_view(dout, dout_str, N, 2) &&
+  const bool direct = d % 8 == 0 && q_str.n == dout_str.n && direct_view(q, q_str, N, 2) &&
+                      direct_view(k, k_str, N, 2) && direct_view(v, v_str, N, 2) && direct_view(dout, dout_str, N, 2) &&
                       direct_view(o, o_str, N, 4) && direct_view(dq, dq_str, N, 4) && direct_view(dk, dk_str, N, 4) &&
                       direct_view(dv, dv_str, N, 4);
   if (direct) {
     const int dp = padded_d(d);
-    const size_t need = fa_bwd_workspace_size(B, H, N, dp, variant);
-    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
-    const Range rw = rng(workspace, need);
-    for (const Range& r : ins)
-      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
-    for (const Range& r : outs)
-      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
     Views vw = contiguous_views(H, N, d);
     vw.q = view_of(q_str);
     vw.k = view_of(k_str);
@@ -741,8 +755,20 @@ fa_status bwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
     vw.dq = view_of(dq_str);
     vw.dk = view_of(dk_str);
     vw.dv = view_of(dv_str);
+    const size_t delta_bytes = fa_bwd_workspace_size(B, H, N, dp, variant);
+    const bool scratch = variant == FA_BWD_5GEMM_ATOMIC && !atomic_dq_in_place(vw, H, N, dp);
+    const size_t need = delta_bytes + (scratch ? align256((size_t)B * H * N * dp * 4) : 0);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+    const Range rw = rng(workspace, need);
+    for (const Range& r : ins)
+      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+    for (const Range& r : outs)
+      if (overlaps(r, rw)) return FA_ERR_INVALID_ARG;
+    char* ws = static_cast<char*>(workspace);
     return bwd_launch(q, k, v, o, lse, dout, B, H, N, dp, causal, scale, variant, dq, dk, dv,
-                      static_cast<float*>(workspace), stream, -1, -1, drop, vw);
+                      reinterpret_cast<float*>(ws), scratch ? reinterpret_cast<float*>(ws + delta_bytes) : nullptr,
+                      stream, -1, -1, drop, vw);
   }
 
   const size_t need = fa_bwd_general_workspace_size(B, H, N, d, variant);

@@ -271,8 +271,7 @@ struct DkdvMath {
   // tile late lets the atomics drain under the next tile's products instead of
   // holding up the end-of-tile wait.
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
-                                                   int N, float scale, int wave, int g, int l32, int lane,
-                                                   long long dq_ld, int hd) {
+                                                   int N, float scale, int wave, int g, int l32, int lane) {
     {
       for (int t = wave; t < QBN * DB; t += NW) {
         const int qb = t / DB, db = t % DB;
@@ -282,20 +281,10 @@ struct DkdvMath {
           acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
                        ColOffsets<D, KMODE>::col_dyn(ktile, ks * 16, db, lane), acc);
         }
-        // in-head element offsets fit 32 bits (N * row pitch < 2^31 is validated): one lane
-        // offset plus a wave-uniform offset per accumulator row.  Both are opaque to the
-        // optimiser, which would otherwise hoist all sixteen row offsets of every
-        // (query block, d block) pair out of the tile loop and hold them in registers.
-        int ld = (int)dq_ld;
-        asm volatile("" : "+s"(ld));
-        const int qlane = q0 + qb * 32 + 4 * g;
-        int lane_off = qlane * ld + db * 32 + l32;
-        asm volatile("" : "+v"(lane_off));
-        const bool col_ok = db * 32 + l32 < hd;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ro = 8 * (r >> 2) + (r & 3);
-          if (qlane + ro < N && col_ok) unsafeAtomicAdd(dqh + (unsigned)(lane_off + ro * ld), acc[r] * scale);
+          const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
         }
       }
     }
@@ -353,9 +342,10 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
   const float* lseh = a.lse + (size_t)bh * N;
   const float* delh = a.delta + (size_t)bh * N;
-  float* dqh = ATOMIC ? a.dq + head_base(a.vdq, bh, a.H) : nullptr;
+  // the atomic dq is a contiguous [B, H, N, D] accumulator (all D columns; past the
+  // head dim they receive zeros, since K is zero there)
+  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * D : nullptr;
   const int hd = a.hd;  // columns hd .. D-1 are zero padding
-  const long long dq_ld = a.vdq.sn;
   const float c = a.scale * kLog2e;
   const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
   const float ks = a.drop_scale;
@@ -366,11 +356,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? k0 / BQ : 0;
   constexpr int KMODE = M::KMODE;
-  TileDMA<BQ, D, NW, kBoth> qdma, ddma;  // Q, dO: row fragments and transposed reads
+  // Q, dO: row fragments and transposed reads; one copier serves both (their row
+  // pitches are equal)
+  TileDMA<BQ, D, NW, kBoth> qdma;
   qdma.init(wave, lane, a.vq.sn, hd);
-  ddma.init(wave, lane, a.vdo.sn, hd);
   qdma.issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
-  ddma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
+  qdma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
   if constexpr (ATOMIC || KV_LDS) {
     TileDMA<BK, D, NW, KMODE> kd;
     kd.init(wave, lane, a.vk.sn, hd);
@@ -421,20 +412,19 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pv.refresh();
     }
     qdma.refresh();
-    ddma.refresh();
     if (it + 1 < nqt) {
       qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
-      ddma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
+      qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
       srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
     if constexpr (ATOMIC && DEFER) {
-      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
+      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
     }
     M::tile(qbuf0, dbuf0, st0, ktile, vtile, dst0, kf, vf, dk, dv, dqh, it * BQ, k0, kw, key, N, c, a.scale, fr, fc,
             pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
-      M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
+      M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
     }
     wait_tile();
     if (it + 1 < nqt) srow.store(st1, N, tid);
@@ -447,18 +437,17 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
       pv.refresh();
     }
     qdma.refresh();
-    ddma.refresh();
     if (it + 2 < nqt) {
       qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
-      ddma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
+      qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
       srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
-    if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
+    if constexpr (ATOMIC && DEFER) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
     M::tile(qbuf1, dbuf1, st1, ktile, vtile, DEFER ? dst1 : dst0, kf, vf, dk, dv, dqh, (it + 1) * BQ, k0, kw, key, N,
             c, a.scale, fr, fc, pk, pv, wave, g, l32, lane, dc, ks);
     if constexpr (ATOMIC && !DEFER) {
       __syncthreads();
-      M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane, dq_ld, hd);
+      M::atomic_dq(dst0, ktile, dqh, (it + 1) * BQ, N, a.scale, wave, g, l32, lane);
     }
     wait_tile();
     if (it + 2 < nqt) srow.store(st0, N, tid);
@@ -466,8 +455,7 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   }
   if constexpr (ATOMIC && DEFER) {  // dQ of the last query tile (its dS^T buffer alternates with the tile's parity)
     const int last = nqt - 1;
-    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane, dq_ld,
-                 hd);
+    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane);
   }
 
   if (key < N) {

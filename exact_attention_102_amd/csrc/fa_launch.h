@@ -49,7 +49,7 @@ struct BwdArgs {
   float scale;
   unsigned drop_k0 = 0, drop_k1 = 0, drop_offset = 0, drop_t = 0;
   float drop_scale = 1.f;
-  View vq{}, vk{}, vv{}, vdo{}, vdq{}, vdk{}, vdv{};
+  View vq{}, vk{}, vv{}, vdo{}, vdq{}, vdk{}, vdv{};  // vdo.sn == vq.sn (one tile copier serves both)
   int hd = 0;
 };
 
