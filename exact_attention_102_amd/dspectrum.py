@@ -4,8 +4,10 @@ for backward pass" (4..96 step 4, ..160 step 8, ..256 step 16, ..384 step 32).
 
     python -m exact_attention_102_amd.dspectrum [--B 4 --H 16 --N 2048] [--out profiles/dspectrum_b4_h16_n2048.md]
 
-Each point runs the general entry points (head dims other than 64/128/256 on
-zero-padded copies at the next built size) on seeded N(0,1) bf16 inputs (the first D columns of one draw), non-causal,
+Each point runs the general entry points on seeded N(0,1) bf16 inputs (the first D
+columns of one draw), non-causal: head dims other than 64/128/256 run on the
+kernels of the next built size, padded inside the kernels when D is a multiple of
+8 and through zero-padded copies otherwise,
 with that page's protocol: 5 trials of 5 back-to-back dispatches, best trial.  It
 reports TFLOP/s credited with the true head dim (4D flop per pair forward, 10D for
 both backward designs), the page's instruction rates ((2D+5) N^2 forward, (3D+5)
@@ -106,7 +108,8 @@ def main():
             fh.write("Best of 5 trials x 5 dispatches.  TFLOP/s credit the true head dim D: 4D (fwd) and 10D (both "
                      "backward designs) flop per pair, peak 2500.  G instr/s: the page's (2D+5) N^2 for the forward "
                      "and (3D+5) N^2 + (4D+5) N^2 for the 7-GEMM backward's two kernels.  Head dims other than "
-                     "64/128/256 run zero-padded at the next built size (`padded`).\n\n")
+                     "64/128/256 run on the kernels of the next built size (`padded`): padded inside the kernels "
+                     "when D is a multiple of 8, through zero-padded copies otherwise.\n\n")
             fh.write("| D | padded | fwd TF | 5-GEMM bwd TF | 7-GEMM bwd TF | fwd G instr/s | 7-GEMM bwd G instr/s | "
                      "t7/t5 | faster bwd |\n|---|---|---|---|---|---|---|---|---|\n")
             for r in rows:

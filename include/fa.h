@@ -146,13 +146,18 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
  * [B,H,N].  Pointers need only element alignment (2 bytes for bf16, 4 for fp32;
  * lse 16 bytes).  The math is that of fa_fwd / fa_bwd; the pages' kernels are
  * built for fixed head dimensions, and issue 1172 asks for arbitrary head
- * dimensions with strided rows, which these entries provide by running the fused
- * kernels at Dp = the smallest of 64, 128, 256 that is >= d on zero-padded
- * contiguous copies held in the workspace (zero columns change no score, so the
- * result is the same attention), then writing the first d columns of the results
- * into the caller's views.  When d is 64, 128 or 256 and every view is contiguous
- * and 16-byte aligned, the call goes straight to fa_fwd / fa_bwd and needs only
- * fa_bwd's workspace.
+ * dimensions with strided rows.  The fused kernels run at Dp = the smallest of 64,
+ * 128, 256 that is >= d, with columns d .. Dp-1 taken as zeros (zero columns change
+ * no score, so the result is the attention of the d columns):
+ *   - in place, reading and writing the caller's views directly, when d is a
+ *     multiple of 8, every base pointer is 16-byte aligned, every stride is a
+ *     multiple of 16 bytes, q and dout share their row stride, and N * stride.n
+ *     stays below 2^31 bytes per view; the kernels pad the head dim themselves and
+ *     touch no element past column d.  The backward then needs the row-term
+ *     workspace of fa_bwd at Dp, plus a [B,H,N,Dp] fp32 dq accumulator for the
+ *     5-GEMM variant unless dq is contiguous with d == Dp;
+ *   - otherwise through zero-padded contiguous copies held in the workspace,
+ *     whose results' first d columns are written into the caller's views.
  * Validation and errors as above; views that overlap an output are rejected
  * (FA_ERR_INVALID_ARG), d outside 1..256 is FA_ERR_UNSUPPORTED. */
 typedef struct {
