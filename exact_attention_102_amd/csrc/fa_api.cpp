@@ -30,7 +30,8 @@ bool overlaps(Range a, Range b) {
 
 Range rng(const void* p, size_t bytes) { return Range{static_cast<const char*>(p), bytes}; }
 
-bool supported_d(int d) { return d == 64 || d == 128 || d == 256; }
+// Head dims with kernels of their own (96 and 192 on 128- and 256-wide tiles).
+bool supported_d(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
 
 // Shared size checks: positive sizes, 32-bit grid and row counts, 64-bit byte counts.
 fa_status check_sizes(int B, int H, int N, int d, float scale) {
@@ -76,13 +77,16 @@ int count_for_d(const Cfg* t, int n, int d) {
 // Default configuration per (pass, d, causal), chosen by the block-shape sweep
 // (exact_attention_102_amd/sweep.py) on the b4_h16_n2048_d128, b4_h8_n4096_d256 and
 // b1_h32_n16384_d64 workloads; an index among the pass's configurations for that d.
+// Head dims 96 and 192 were chosen on B4 H16 N2048 (both masks).
 int default_index(int pass, int d, int causal) {
   switch (pass) {
-    case 0: return d == 64 ? 2 : 0;                   // fwd: d64 Br32x8 Bc64, d128 Br32x4 Bc64, d256 Bc32
+    case 0:  // fwd: d64 Br32x8 Bc64, d96 Br32x8 Bc64, d128 Br32x4 Bc64, d192 Bc64 (causal Bc32), d256 Bc32
+      return d == 64 ? 2 : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
     case 1: return d == 64 ? 2 : (d == 128 && causal) ? 3 : 0;  // dkdv: d64 Bk32x8 Bq64, d128 Bk32x4 Bq64
                                                                  // (causal: K/V in LDS)
     case 2: return d == 64 ? 3 : 0;                   // dkdv + atomic dq: d64 Bk32x8 Bq64 deferred
-    case 3: return (d == 128 && !causal) ? 2 : 0;     // dq: d128 non-causal Bq32x8 Bc64
+    case 3:                                           // dq: d128 non-causal Bq32x8 Bc64, d96 causal Bq32x8
+      return ((d == 128 && !causal) ? 2 : 0) + ((d == 96 && causal) ? 1 : 0);
     default: return -1;
   }
 }
@@ -562,7 +566,7 @@ namespace {
 
 constexpr int kMaxGeneralD = 256;
 
-int padded_d(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+int padded_d(int d) { return d <= 64 ? 64 : (d <= 96 ? 96 : (d <= 128 ? 128 : (d <= 192 ? 192 : 256))); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 

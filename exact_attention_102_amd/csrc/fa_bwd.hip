@@ -66,9 +66,11 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
 }
 
 int launch_preprocess(const PreArgs& a, int d, hipStream_t stream) {
-  const int rpb = 256 / (d / 8);
+  // head dims 96 and 192 run on the 128- and 256-wide row kernels (a.hd masks the rest)
+  const int kd = d == 96 ? 128 : (d == 192 ? 256 : d);
+  const int rpb = 256 / (kd / 8);
   const int blocks = (a.rows + rpb - 1) / rpb;
-  switch (d) {
+  switch (kd) {
     case 64: hipLaunchKernelGGL(preprocess_kernel<64>, dim3(blocks), dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(preprocess_kernel<128>, dim3(blocks), dim3(256), 0, stream, a); break;
     case 256: hipLaunchKernelGGL(preprocess_kernel<256>, dim3(blocks), dim3(256), 0, stream, a); break;
@@ -118,14 +120,16 @@ struct RowStager {
 // (query block, d block) pairs) and adds it to dq with fp32 atomics, one atomic
 // per dq element per workgroup and query tile.
 // KV_LDS keeps the workgroup's K and V in LDS instead of registers (large d).
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DROP>
+// D: LDS tile width (64, 128, 256); DV <= D (a multiple of 32): the head-dim columns
+// computed (96 and 192 run on 128- and 256-wide tiles without the zero columns' products).
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DROP>
 struct DkdvMath {
   // K tile: plain row fragments (KV_LDS) and/or transposed reads (atomic dQ product)
   static constexpr int KMODE = ATOMIC ? (KV_LDS ? kBoth : kColOnly) : kRowOnly;
   static constexpr int BK = 32 * NW;
   static constexpr int QBN = BQ / 32;
-  static constexpr int DB = D / 32;
-  static constexpr int KK = D / 16;
+  static constexpr int DB = DV / 32;
+  static constexpr int KK = DV / 16;
   // LDS fragment reads issued ahead of their MFMAs (needs registers the d = 256 and
   // the 8-wave atomic shapes do not have; those keep short scheduling fences)
   static constexpr bool kReadAhead = D <= 128 && !(ATOMIC && NW > 4);
@@ -284,7 +288,7 @@ struct DkdvMath {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
+          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * DV + db * 32 + l32, acc[r] * scale);
         }
       }
     }
@@ -293,9 +297,9 @@ struct DkdvMath {
 
 // DEFER (atomic only): the dQ product and atomics of a query tile run at the start
 // of the next tile, from a second dS^T buffer, instead of behind an extra barrier.
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER, bool DROP>
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER, bool DROP>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
-  using M = DkdvMath<D, BQ, NW, CAUSAL, ATOMIC, KV_LDS, DROP>;
+  using M = DkdvMath<D, DV, BQ, NW, CAUSAL, ATOMIC, KV_LDS, DROP>;
   constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
   constexpr int NT = NW * 64;
   constexpr int QTILE = BQ * D * 2;
@@ -342,9 +346,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
   const float* lseh = a.lse + (size_t)bh * N;
   const float* delh = a.delta + (size_t)bh * N;
-  // the atomic dq is a contiguous [B, H, N, D] accumulator (all D columns; past the
+  // the atomic dq is a contiguous [B, H, N, DV] accumulator (all DV columns; past the
   // head dim they receive zeros, since K is zero there)
-  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * D : nullptr;
+  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * DV : nullptr;
   const int hd = a.hd;  // columns hd .. D-1 are zero padding
   const float c = a.scale * kLog2e;
   const DropCtx dc{a.drop_k0, a.drop_k1, (unsigned)bh, a.drop_offset, a.drop_t};
@@ -489,11 +493,11 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T                 A = transposed reads of the K tile
 // No atomics: each dq element is written once, so results are reproducible bit
 // for bit (issue 1172: the 7-GEMM form is deterministic).
-template <int D, int BC, bool CAUSAL, bool DROP>
+template <int D, int DV, int BC, bool CAUSAL, bool DROP>
 struct DqMath {
   static constexpr int KB = BC / 32;
-  static constexpr int DB = D / 32;
-  static constexpr int KK = D / 16;
+  static constexpr int DB = DV / 32;
+  static constexpr int KK = DV / 16;
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               const bf16x8 (&dof)[KK], f32x16 (&dq)[DB], float lse2, float dl,
                                               int k0, int q_w, int qi, int N, float c,
@@ -540,9 +544,9 @@ struct DqMath {
   }
 };
 
-template <int D, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
+template <int D, int DV, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
-  using M = DqMath<D, BC, CAUSAL, DROP>;
+  using M = DqMath<D, DV, BC, CAUSAL, DROP>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;
   constexpr int DB = M::DB, KK = M::KK;
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false, bool DROP = false>
+template <int D, int DV, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false, bool DROP = false>
 static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 32 * NW;
   const int nkt = (a.N + BK - 1) / BK;
@@ -665,16 +669,16 @@ static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, true, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, true, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
                        dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, BQ, NW, false, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, false, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
                        dim3(NW * 64), 0, stream, a);
   }
   return 0;
 }
 
-template <int D, int BC, int NW, int OCC, bool DROP = false>
+template <int D, int DV, int BC, int NW, int OCC, bool DROP = false>
 static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
@@ -682,37 +686,59 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((dq_kernel<D, DV, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dq_kernel<D, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((dq_kernel<D, DV, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   }
   return 0;
 }
 
 #define DKDV_CFG(D, BQ, NW, KVL) \
-  { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, false, KVL> }
-#define DKDVA_CFG(D, BQ, NW, KVL) \
-  { D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, BQ, NW, true, KVL> }
+  { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, D, BQ, NW, false, KVL> }
+#define DKDVA_CFG(D, BQ, NW, KVL)                                                                        \
+  {                                                                                                        \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                   \
+        &launch_dkdv<D, D, BQ, NW, true, KVL>                                                              \
+  }
 #define DKDVAD_CFG(D, BQ, NW, KVL)                                                                       \
   {                                                                                                        \
     D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " deferred",         \
-        &launch_dkdv<D, BQ, NW, true, KVL, true>                                                           \
+        &launch_dkdv<D, D, BQ, NW, true, KVL, true>                                                        \
   }
 #define DQ_CFG(D, BC, NW, OCC) \
-  { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC> }
-#define DKDV_DROP_CFG(D, BQ, NW, KVL)                                                                   \
-  {                                                                                                       \
-    D, 32 * (NW), BQ, NW, "dkdv+dropout d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                     \
-        &launch_dkdv<D, BQ, NW, false, KVL, false, true>                                                  \
+  { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, D, BC, NW, OCC> }
+// head dim DV on D-wide tiles (the table's key is DV)
+#define DKDV_CFGV(D, DV, BQ, NW, KVL)                                                                   \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,            \
+        &launch_dkdv<D, DV, BQ, NW, false, KVL>                                                            \
   }
-#define DKDVA_DROP_CFG(D, BQ, NW, KVL, DEF)                                                             \
-  {                                                                                                       \
-    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " defer" #DEF, \
-        &launch_dkdv<D, BQ, NW, true, KVL, DEF, true>                                                     \
+#define DKDVA_CFGV(D, DV, BQ, NW, KVL)                                                                  \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,  \
+        &launch_dkdv<D, DV, BQ, NW, true, KVL>                                                             \
   }
-#define DQ_DROP_CFG(D, BC, NW, OCC) \
-  { D, 32 * (NW), BC, NW, "dq+dropout d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, BC, NW, OCC, true> }
+#define DQ_CFGV(D, DV, BC, NW, OCC)                                                                     \
+  {                                                                                                        \
+    DV, 32 * (NW), BC, NW, "dq d" #DV " (tiles " #D ") Bq32x" #NW " Bc" #BC " occ" #OCC,                 \
+        &launch_dq<D, DV, BC, NW, OCC>                                                                     \
+  }
+#define DKDV_DROP_CFG(D, DV, BQ, NW, KVL)                                                               \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv+dropout d" #DV " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                    \
+        &launch_dkdv<D, DV, BQ, NW, false, KVL, false, true>                                               \
+  }
+#define DKDVA_DROP_CFG(D, DV, BQ, NW, KVL, DEF)                                                         \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #DV " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " defer" #DEF, \
+        &launch_dkdv<D, DV, BQ, NW, true, KVL, DEF, true>                                                  \
+  }
+#define DQ_DROP_CFG(D, DV, BC, NW, OCC)                                                                 \
+  {                                                                                                        \
+    DV, 32 * (NW), BC, NW, "dq+dropout d" #DV " Bq32x" #NW " Bc" #BC " occ" #OCC,                         \
+        &launch_dq<D, DV, BC, NW, OCC, true>                                                               \
+  }
 
 const BwdConfig* dkdv_configs(int* count) {
   static const BwdConfig table[] = {
@@ -720,6 +746,7 @@ const BwdConfig* dkdv_configs(int* count) {
       DKDV_CFG(128, 64, 4, false), DKDV_CFG(128, 32, 4, false), DKDV_CFG(128, 32, 4, true),
       DKDV_CFG(128, 64, 4, true),  DKDV_CFG(128, 32, 2, true),
       DKDV_CFG(256, 32, 2, true),
+      DKDV_CFGV(128, 96, 64, 4, false), DKDV_CFGV(128, 96, 64, 4, true), DKDV_CFGV(256, 192, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -731,6 +758,7 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       DKDVAD_CFG(64, 64, 8, false),
       DKDVA_CFG(128, 64, 4, false), DKDVA_CFG(128, 32, 4, false), DKDVAD_CFG(128, 64, 4, false),
       DKDVA_CFG(256, 32, 2, true),
+      DKDVA_CFGV(128, 96, 64, 4, false), DKDVA_CFGV(256, 192, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -741,6 +769,7 @@ const BwdConfig* dq_configs(int* count) {
       DQ_CFG(64, 64, 4, 2),  DQ_CFG(64, 128, 4, 2), DQ_CFG(64, 64, 8, 2),
       DQ_CFG(128, 64, 4, 2), DQ_CFG(128, 32, 4, 2), DQ_CFG(128, 64, 8, 2),
       DQ_CFG(256, 32, 4, 1), DQ_CFG(256, 64, 4, 1),
+      DQ_CFGV(128, 96, 64, 4, 2), DQ_CFGV(128, 96, 64, 8, 2), DQ_CFGV(256, 192, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -749,7 +778,8 @@ const BwdConfig* dq_configs(int* count) {
 // Dropout: the non-causal default shape of each head dim.
 const BwdConfig* dkdv_dropout_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDV_DROP_CFG(64, 64, 8, false), DKDV_DROP_CFG(128, 64, 4, false), DKDV_DROP_CFG(256, 32, 2, true),
+      DKDV_DROP_CFG(64, 64, 64, 8, false),  DKDV_DROP_CFG(128, 128, 64, 4, false), DKDV_DROP_CFG(256, 256, 32, 2, true),
+      DKDV_DROP_CFG(128, 96, 64, 4, false), DKDV_DROP_CFG(256, 192, 32, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -757,8 +787,9 @@ const BwdConfig* dkdv_dropout_configs(int* count) {
 
 const BwdConfig* dkdv_atomic_dropout_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDVA_DROP_CFG(64, 64, 4, false, false), DKDVA_DROP_CFG(128, 64, 4, false, false),
-      DKDVA_DROP_CFG(256, 32, 2, true, false),
+      DKDVA_DROP_CFG(64, 64, 64, 4, false, false),  DKDVA_DROP_CFG(128, 128, 64, 4, false, false),
+      DKDVA_DROP_CFG(256, 256, 32, 2, true, false), DKDVA_DROP_CFG(128, 96, 64, 4, false, false),
+      DKDVA_DROP_CFG(256, 192, 32, 2, true, false),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -766,7 +797,8 @@ const BwdConfig* dkdv_atomic_dropout_configs(int* count) {
 
 const BwdConfig* dq_dropout_configs(int* count) {
   static const BwdConfig table[] = {
-      DQ_DROP_CFG(64, 64, 4, 2), DQ_DROP_CFG(128, 64, 8, 2), DQ_DROP_CFG(256, 32, 4, 1),
+      DQ_DROP_CFG(64, 64, 64, 4, 2), DQ_DROP_CFG(128, 128, 64, 8, 2), DQ_DROP_CFG(256, 256, 32, 4, 1),
+      DQ_DROP_CFG(128, 96, 64, 8, 2), DQ_DROP_CFG(256, 192, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

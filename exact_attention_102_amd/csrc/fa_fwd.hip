@@ -37,11 +37,14 @@ namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D, int BC, bool CAUSAL, bool DROP>
+// D: width of the LDS tiles (64, 128, 256); DV <= D, a multiple of 32: the head-dim
+// columns actually computed (96 and 192 run on 128- and 256-wide tiles and skip the
+// products of the zero columns).
+template <int D, int DV, int BC, bool CAUSAL, bool DROP>
 struct FwdTileMath {
   static constexpr int KB = BC / 32;  // 32-key blocks per tile
-  static constexpr int DB = D / 32;   // 32-wide blocks of the head dim
-  static constexpr int KK = D / 16;   // k-steps of Q K^T
+  static constexpr int DB = DV / 32;  // 32-wide blocks of the computed head dim
+  static constexpr int KK = DV / 16;  // k-steps of Q K^T
   static constexpr int kAhead = 3;
   static constexpr int kAheadV = 3;
 
@@ -145,9 +148,9 @@ struct FwdTileMath {
 
 // OCC: waves per SIMD the register allocation must allow (2 lets a second wave's
 // MFMAs overlap this wave's softmax; d = 256 needs the whole register file).
-template <int D, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
+template <int D, int DV, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
-  using M = FwdTileMath<D, BC, CAUSAL, DROP>;
+  using M = FwdTileMath<D, DV, BC, CAUSAL, DROP>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;  // bytes of one K or V tile
   constexpr int DB = M::DB, KK = M::KK;
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int BC, int NW, int OCC, bool DROP = false>
+template <int D, int DV, int BC, int NW, int OCC, bool DROP = false>
 static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
@@ -263,19 +266,28 @@ static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<D, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   }
   return 0;
 }
 
 #define FWD_CFG(D, BC, NW, OCC) \
-  { D, 32 * (NW), BC, NW, "fwd d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, BC, NW, OCC> }
-#define FWD_DROP_CFG(D, BC, NW, OCC) \
-  { D, 32 * (NW), BC, NW, "fwd+dropout d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, BC, NW, OCC, true> }
+  { D, 32 * (NW), BC, NW, "fwd d" #D " Br32x" #NW " Bc" #BC " occ" #OCC, &launch_fwd<D, D, BC, NW, OCC> }
+// head dim DV on D-wide tiles (the table's key is DV)
+#define FWD_CFGV(D, DV, BC, NW, OCC)                                                                    \
+  {                                                                                                       \
+    DV, 32 * (NW), BC, NW, "fwd d" #DV " (tiles " #D ") Br32x" #NW " Bc" #BC " occ" #OCC,               \
+        &launch_fwd<D, DV, BC, NW, OCC>                                                                   \
+  }
+#define FWD_DROP_CFG(D, DV, BC, NW, OCC)                                                                \
+  {                                                                                                       \
+    DV, 32 * (NW), BC, NW, "fwd+dropout d" #DV " Br32x" #NW " Bc" #BC " occ" #OCC,                     \
+        &launch_fwd<D, DV, BC, NW, OCC, true>                                                             \
+  }
 
 // Host-side table (function-local so that only the host pass materialises it).
 const FwdConfig* fwd_configs(int* count) {
@@ -283,6 +295,8 @@ const FwdConfig* fwd_configs(int* count) {
       FWD_CFG(64, 64, 4, 2),   FWD_CFG(64, 128, 4, 2),  FWD_CFG(64, 64, 8, 2),  FWD_CFG(64, 128, 8, 2),
       FWD_CFG(128, 64, 4, 2),  FWD_CFG(128, 32, 4, 2),  FWD_CFG(128, 64, 8, 2), FWD_CFG(128, 128, 4, 1),
       FWD_CFG(256, 32, 4, 1),  FWD_CFG(256, 64, 4, 1),
+      FWD_CFGV(128, 96, 64, 4, 2), FWD_CFGV(128, 96, 64, 8, 2), FWD_CFGV(256, 192, 32, 4, 1),
+      FWD_CFGV(256, 192, 64, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -290,7 +304,8 @@ const FwdConfig* fwd_configs(int* count) {
 
 const FwdConfig* fwd_dropout_configs(int* count) {
   static const FwdConfig table[] = {
-      FWD_DROP_CFG(64, 64, 8, 2), FWD_DROP_CFG(128, 64, 4, 2), FWD_DROP_CFG(256, 32, 4, 1),
+      FWD_DROP_CFG(64, 64, 64, 8, 2),   FWD_DROP_CFG(128, 128, 64, 4, 2), FWD_DROP_CFG(256, 256, 32, 4, 1),
+      FWD_DROP_CFG(128, 96, 64, 4, 2),  FWD_DROP_CFG(256, 192, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

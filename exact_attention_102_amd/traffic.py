@@ -84,16 +84,16 @@ def classify(name: str):
     if not m:
         return None
     kind, targs = m.group(1), [t.strip() for t in m.group(2).split(",")]
-    # template arguments: fwd / dq <D, tile, waves, occupancy, CAUSAL, DROP>;
-    # dkdv <D, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>; dropout kernels are not classified
+    # template arguments: fwd / dq <D, DV, tile, waves, occupancy, CAUSAL, DROP>;
+    # dkdv <D, DV, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>; dropout kernels are not classified
     if targs[-1] == "true" and kind in ("fwd", "dq", "dkdv"):
         return None
     if kind == "fwd":
-        return "fwd", ("causal" if targs[4] == "true" else "full")
+        return "fwd", ("causal" if targs[5] == "true" else "full")
     if kind == "dq":
-        return "dq", ("causal" if targs[4] == "true" else "full")
+        return "dq", ("causal" if targs[5] == "true" else "full")
     if kind == "dkdv":
-        causal, atomic = targs[3] == "true", targs[4] == "true"
+        causal, atomic = targs[4] == "true", targs[5] == "true"
         return ("dkdv_atomic" if atomic else "dkdv"), ("causal" if causal else "full")
     if kind == "preprocess":
         return "preprocess", None

@@ -33,7 +33,7 @@
  *             nothing is launched and outputs are untouched.  FA_ERR_INVALID_ARG:
  *             null/misaligned pointer, B, H or N <= 0, non-finite or non-positive
  *             scale, aliasing, or a tensor too large for 32-bit in-head indexing;
- *             FA_ERR_UNSUPPORTED: head dim not in {64, 128, 256} or unknown
+ *             FA_ERR_UNSUPPORTED: head dim not in {64, 96, 128, 192, 256} or unknown
  *             variant/config; FA_ERR_WORKSPACE: workspace missing or too small;
  *             FA_ERR_HIP: a launch failed (hipGetLastError after the launch).
  *  Threads    stateless apart from a once-initialised device-property cache;

@@ -21,7 +21,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
 SMALL = [(1, 2, 1), (1, 1, 33), (1, 2, 77), (2, 2, 300), (1, 2, 512)]
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("bhn", SMALL, ids=lambda t: "B%dH%dN%d" % t)
 def test_small_fwd_bwd(d, causal, bhn):
@@ -43,7 +43,7 @@ def _all_cfgs(pass_id, d):
     return list(range(fa_num_configs(pass_id, d)))
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_tile_config(d, causal):
     from exact_attention_102_amd import PASS_DKDV, PASS_DKDV_ATOMIC, PASS_DQ, PASS_FWD
@@ -100,7 +100,7 @@ def test_sharp_softmax_small():
             check_backward(gpu_backward(dev, o, lse, causal, scale, var), refs)
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 def test_causal_row_zero_is_v0(d):
     B, H, N = 2, 2, 200
     scale = 1.0 / math.sqrt(d)
@@ -116,7 +116,7 @@ def test_causal_row_zero_is_v0(d):
     assert np.max(np.abs(lse[:, :, 0].cpu().numpy() - want)) <= 1e-5
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 def test_7gemm_is_bitwise_deterministic(d):
     B, H, N = 2, 2, 333
     scale = 1.0 / math.sqrt(d)

@@ -43,7 +43,7 @@ def run(dev, causal, scale, p, seed, offset, variants=VARIANTS):
     return o, lse, grads
 
 
-@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("bhn,p", [((1, 1, 1), 0.3), ((1, 2, 77), 0.1), ((2, 2, 300), 0.5)],
                          ids=lambda x: ("B%dH%dN%d" % x) if isinstance(x, tuple) else "p%g" % x)
