@@ -208,7 +208,7 @@ int fa_default_config(int pass, int d, int causal) {
 
 namespace {
 
-// The forward's launch on validated views: kernels built for head dim D (64, 128, 256),
+// The forward's launch on validated views: kernels built for head dim D (64, 96, 128, 192, 256),
 // tensors with head dim vw.hd <= D.  With dropout (drop->t != 0) the dropout table's
 // shape for D runs and cfg is ignored.
 fa_status fwd_launch(const void* q, const void* k, const void* v, float* o, float* lse, int B, int H, int N, int D,

@@ -12,7 +12,7 @@ struct View {
 };
 
 // Every tensor is passed as a base pointer plus a View; hd is the tensors' head
-// dim.  The kernels are built for D = 64, 128, 256 >= hd: columns hd .. D-1 read as
+// dim.  The kernels are built for D = 64, 96, 128, 192, 256 >= hd: columns hd .. D-1 read as
 // zeros (the tile copies and register loads fetch nothing there) and are never
 // written, so the result is the attention of the hd columns (zero columns change
 // no score).  Row starts are 16-byte aligned and hd is a multiple of 8.

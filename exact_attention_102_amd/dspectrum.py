@@ -5,9 +5,9 @@ for backward pass" (4..96 step 4, ..160 step 8, ..256 step 16, ..384 step 32).
     python -m exact_attention_102_amd.dspectrum [--B 4 --H 16 --N 2048] [--out profiles/dspectrum_b4_h16_n2048.md]
 
 Each point runs the general entry points on seeded N(0,1) bf16 inputs (the first D
-columns of one draw), non-causal: head dims other than 64/128/256 run on the
-kernels of the next built size, padded inside the kernels when D is a multiple of
-8 and through zero-padded copies otherwise,
+columns of one draw), non-causal: head dims other than the built 64/96/128/192/256
+run on the kernels of the next built size, padded inside the kernels when D is a
+multiple of 8 and through zero-padded copies otherwise,
 with that page's protocol: 5 trials of 5 back-to-back dispatches, best trial.  It
 reports TFLOP/s credited with the true head dim (4D flop per pair forward, 10D for
 both backward designs), the page's instruction rates ((2D+5) N^2 forward, (3D+5)
@@ -86,7 +86,7 @@ def main():
         t_5, _ = time_calls(bwd(FA_BWD_5GEMM_ATOMIC), torch)
         t_7, _ = time_calls(bwd(FA_BWD_7GEMM), torch)
         rec.update({
-            "supported": True, "padded_to": 64 if D <= 64 else (128 if D <= 128 else 256),
+            "supported": True, "padded_to": min(b for b in (64, 96, 128, 192, 256) if b >= D),
             "fwd_ms": round(t_f, 4), "bwd5_ms": round(t_5, 4), "bwd7_ms": round(t_7, 4),
             "fwd_tflops": round(fl["fwd"] / t_f / 1e9, 1),
             "bwd5_tflops": round(fl["bwd_effective"] / t_5 / 1e9, 1),
@@ -108,7 +108,7 @@ def main():
             fh.write("Best of 5 trials x 5 dispatches.  TFLOP/s credit the true head dim D: 4D (fwd) and 10D (both "
                      "backward designs) flop per pair, peak 2500.  G instr/s: the page's (2D+5) N^2 for the forward "
                      "and (3D+5) N^2 + (4D+5) N^2 for the 7-GEMM backward's two kernels.  Head dims other than "
-                     "64/128/256 run on the kernels of the next built size (`padded`): padded inside the kernels "
+                     "64/96/128/192/256 run on the kernels of the next built size (`padded`): padded inside the kernels "
                      "when D is a multiple of 8, through zero-padded copies otherwise.\n\n")
             fh.write("| D | padded | fwd TF | 5-GEMM bwd TF | 7-GEMM bwd TF | fwd G instr/s | 7-GEMM bwd G instr/s | "
                      "t7/t5 | faster bwd |\n|---|---|---|---|---|---|---|---|---|\n")

@@ -147,7 +147,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
  * lse 16 bytes).  The math is that of fa_fwd / fa_bwd; the pages' kernels are
  * built for fixed head dimensions, and issue 1172 asks for arbitrary head
  * dimensions with strided rows.  The fused kernels run at Dp = the smallest of 64,
- * 128, 256 that is >= d, with columns d .. Dp-1 taken as zeros (zero columns change
+ * 96, 128, 192, 256 that is >= d, with columns d .. Dp-1 taken as zeros (zero columns change
  * no score, so the result is the attention of the d columns):
  *   - in place, reading and writing the caller's views directly, when d is a
  *     multiple of 8, every base pointer is 16-byte aligned, every stride is a
@@ -200,7 +200,7 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
  * The forward computes o = (P * M * s) v with lse that of the undropped scores;
  * the backward gives the gradients of sum(dout * o) for that same mask, redrawn
  * from (seed, offset): pass the forward's values.  A p that rounds to t = 0 runs the
- * plain kernels.  Head dims 64, 128, 256 here (any d in 1..256 through the general
+ * plain kernels.  Head dims 64, 96, 128, 192, 256 here (any d in 1..256 through the general
  * dropout entries below); each pass runs one tile shape per head dim.
  * Errors as above; p outside [0, 1) or not finite is FA_ERR_INVALID_ARG. */
 typedef struct {
