@@ -297,6 +297,7 @@ const FwdConfig* fwd_configs(int* count) {
       FWD_CFG(256, 32, 4, 1),  FWD_CFG(256, 64, 4, 1),
       FWD_CFGV(128, 96, 64, 4, 2), FWD_CFGV(128, 96, 64, 8, 2), FWD_CFGV(256, 192, 32, 4, 1),
       FWD_CFGV(256, 192, 64, 4, 1),
+      FWD_CFG(128, 32, 4, 3),  FWD_CFG(64, 64, 4, 3),  FWD_CFG(64, 32, 4, 4), FWD_CFGV(128, 96, 32, 4, 3),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
