@@ -133,6 +133,10 @@ struct DkdvMath {
   // LDS fragment reads issued ahead of their MFMAs (needs registers the d = 256 and
   // the 8-wave atomic shapes do not have; those keep short scheduling fences)
   static constexpr bool kReadAhead = D <= 128 && !(ATOMIC && NW > 4);
+  // Software pipelining across the tile's query blocks (see tile()): measured faster
+  // only at d = 64 (8-wave dK/dV +8%, 4-wave atomic +15%); the d = 128 shapes lose
+  // 7-14% and the 8-wave atomic shapes run out of registers.
+  static constexpr bool kPipe = !DROP && QBN >= 2 && D == 64 && DV == 64 && !(ATOMIC && NW > 4);
 
   __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
@@ -144,6 +148,116 @@ struct DkdvMath {
                                               int lane, const DropCtx& dc, float ks) {
     const LDS float* l2t = stats;
     const LDS float* dlt = stats + BQ;
+    // Pipelined path (kPipe shapes): every query block of the tile is inside the
+    // sequence and below the causal diagonal for all of this wave's keys (no mask).
+    // The S / dP products of block qb + 1 are issued between the exp / dS arithmetic
+    // of block qb, so the wave overlaps its own VALU work with its MFMAs.
+    if constexpr (kPipe) {
+      if (q0 + BQ <= N && (!CAUSAL || q0 >= kw + 31)) {
+        f32x16 sc = zero16(), dpc = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          bf16x8 kb, vb;
+          if constexpr (KV_LDS) {
+            kb = pk.row(ktile, wave * 32, kk);
+            vb = pv.row(vtile, wave * 32, kk);
+          } else {
+            kb = kf[kk];
+            vb = vf[kk];
+          }
+          sc = mfma32(fr.row(qtl, 0, kk), kb, sc);
+          dpc = mfma32(fr.row(dotl, 0, kk), vb, dpc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int qb = 0; qb < QBN; ++qb) {
+          float l2[16], dl[16];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int r = qb * 32 + 16 * h + 8 * g + 4 * hf;
+              const f32x4 lv = *(const LDS f32x4*)(l2t + r);
+              const f32x4 dd = *(const LDS f32x4*)(dlt + r);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                l2[8 * h + 4 * hf + e] = lv[e];
+                dl[8 * h + 4 * hf + e] = dd[e];
+              }
+            }
+          }
+          f32x16 sn = zero16(), dpn = zero16();
+          if (qb + 1 < QBN) {
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+              bf16x8 kb, vb;
+              if constexpr (KV_LDS) {
+                kb = pk.row(ktile, wave * 32, kk);
+                vb = pv.row(vtile, wave * 32, kk);
+              } else {
+                kb = kf[kk];
+                vb = vf[kk];
+              }
+              sn = mfma32(fr.row(qtl, (qb + 1) * 32, kk), kb, sn);
+              dpn = mfma32(fr.row(dotl, (qb + 1) * 32, kk), vb, dpn);
+            }
+          }
+          f32x16 p, ds;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv_ = exp2_hw(fmaf(sc[r], c, -l2[r]));
+            p[r] = pv_;
+            ds[r] = pv_ * (dpc[r] - dl[r]);
+          }
+          const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+          bf16x8 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
+          if (qb + 1 < QBN) {
+            // stats reads, then each of the 2 KK products with its fragment read and a
+            // share of the exp / dS arithmetic
+            __builtin_amdgcn_sched_group_barrier(0x100, 8 + 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KK; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
+            dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+            if constexpr (!kReadAhead) fence_every<2>(db);
+          }
+          if constexpr (kReadAhead) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int db = 0; db < DB - 1; ++db) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
+          if constexpr (ATOMIC) {
+            if (!CAUSAL && key >= N) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                sb0[e] = (__bf16)0.f;
+                sb1[e] = (__bf16)0.f;
+              }
+            }
+            *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 8 * g)) = sb0;
+            *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = sb1;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          sc = sn;
+          dpc = dpn;
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int qb = 0; qb < QBN; ++qb) {
       const int qbase = q0 + qb * 32;
