@@ -134,9 +134,11 @@ struct DkdvMath {
   // the 8-wave atomic shapes do not have; those keep short scheduling fences)
   static constexpr bool kReadAhead = D <= 128 && !(ATOMIC && NW > 4);
   // Software pipelining across the tile's query blocks (see tile()): measured faster
-  // only at d = 64 (8-wave dK/dV +8%, 4-wave atomic +15%); the d = 128 shapes lose
-  // 7-14% and the 8-wave atomic shapes run out of registers.
-  static constexpr bool kPipe = !DROP && QBN >= 2 && D == 64 && DV == 64 && !(ATOMIC && NW > 4);
+  // only for two d = 64 shapes (8-wave dK/dV +8%, 4-wave atomic +15%); the 4-wave
+  // dK/dV loses 17%, the d = 128 shapes 7-14%, and the 8-wave atomic shapes run out
+  // of registers.
+  static constexpr bool kPipe =
+      !DROP && QBN >= 2 && D == 64 && DV == 64 && (ATOMIC ? NW == 4 : NW == 8);
 
   __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
