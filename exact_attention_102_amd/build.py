@@ -3,8 +3,8 @@
     python -m exact_attention_102_amd.build        # or __graft_entry__.build()
 
 Each translation unit is compiled by hipcc for gfx950 in parallel, then linked
-into exact_attention_102_amd/libfa.so; the stand-alone atomic-throughput probe
-(csrc/probe_atomic_dq.hip) is built next to it.
+into exact_attention_102_amd/libfa.so; the stand-alone measurement probes
+(csrc/probe_atomic_dq.hip, csrc/probe_rates.hip) are built next to it.
 """
 from __future__ import annotations
 
@@ -21,9 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_pad.hip", "fa_api.cpp"]
-# measurement tool, not part of libfa.so
-PROBE_SRC = "probe_atomic_dq.hip"
-PROBE_PATH = os.path.join(PKG, "probe_atomic_dq")
+# measurement tools (stand-alone programs), not part of libfa.so
+PROBES = ["probe_atomic_dq", "probe_rates"]
 ARCH = "gfx950"
 # Packed-fp32 instructions are disabled: the compiler must not emit v_pk_{add,mul,fma}_f32.
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
@@ -65,15 +64,16 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
-def build_probe(verbose: bool = False) -> str:
-    """Builds the stand-alone dQ-atomic throughput probe (csrc/probe_atomic_dq.hip)."""
-    cmd = [hipcc()] + FLAGS + ["-x", "hip", os.path.join(CSRC, PROBE_SRC), "-o", PROBE_PATH]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError("building the atomic probe failed:\n%s" % r.stderr)
-    return PROBE_PATH
+def build_probe(verbose: bool = False) -> None:
+    """Builds the stand-alone measurement probes (csrc/probe_*.hip) next to the library."""
+    for name in PROBES:
+        cmd = [hipcc()] + FLAGS + ["-I" + CSRC, "-x", "hip", os.path.join(CSRC, name + ".hip"), "-o",
+                                   os.path.join(PKG, name)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError("building %s failed:\n%s" % (name, r.stderr))
 
 
 if __name__ == "__main__":
