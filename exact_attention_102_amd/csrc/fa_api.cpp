@@ -563,7 +563,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
-// General entry points (any d in 1..256, strided views): padded contiguous copies.
+// General entry points (any d in 1..256, strided views): in place when the kernels can read the
+// views directly, otherwise through zero-padded contiguous copies.
 namespace {
 
 constexpr int kMaxGeneralD = 256;
