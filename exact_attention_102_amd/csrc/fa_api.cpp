@@ -80,13 +80,18 @@ int count_for_d(const Cfg* t, int n, int d) {
 // Head dims 96 and 192 were chosen on B4 H16 N2048 (both masks).
 int default_index(int pass, int d, int causal) {
   switch (pass) {
-    case 0:  // fwd: d64 Br32x8 Bc64, d96 Br32x8 Bc64, d128 Br32x4 Bc64, d192 Bc64, d256 Bc32; causal d96 and
-             // d128 Br32x4 Bc32 at three waves per SIMD, causal d192 Bc32
-      if (causal && (d == 96 || d == 128)) return d == 96 ? 2 : 4;
-      return d == 64 ? 2 : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
-    case 1: return d == 64 ? 2 : (d == 128 && causal) ? 3 : 0;  // dkdv: d64 Bk32x8 Bq64, d128 Bk32x4 Bq64
-                                                                 // (causal: K/V in LDS)
-    case 2: return d == 64 ? 3 : 0;                   // dkdv + atomic dq: d64 Bk32x8 Bq64 deferred
+    case 0:  // fwd: d64 Br32x4 Bc64 at three waves per SIMD (causal: Br32x8 Bc64), d96 Br32x8 Bc64, d128
+             // Br32x4 Bc32 at three waves per SIMD, d192 Bc64, d256 Bc32; causal d96 Br32x4 Bc32 at three
+             // waves per SIMD, causal d192 Bc32
+      if (d == 128) return 4;
+      if (causal && d == 96) return 2;
+      return d == 64 ? (causal ? 2 : 4) : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
+    case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d96 and d128 Bk32x4 Bq64, d192 and d256 Bk32x4
+             // Bq32, K read from LDS
+      return d == 64 ? 2 : d == 96 ? 2 : d == 128 ? 5 : 1;
+    case 2:  // dkdv + atomic dq, K read from LDS, dQ one tile late: d64 Bk32x8 Bq64, d96 and d128 Bk32x8
+             // Bq32, d192 and d256 Bk32x4 Bq32
+      return d == 64 ? 4 : d == 128 ? 3 : 1;
     case 3:                                           // dq: d128 non-causal Bq32x8 Bc64, d96 causal Bq32x8
       return ((d == 128 && !causal) ? 2 : 0) + ((d == 96 && causal) ? 1 : 0);
     default: return -1;

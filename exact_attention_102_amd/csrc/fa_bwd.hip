@@ -112,20 +112,24 @@ struct RowStager {
 // double-buffered LDS, the Q/dO rows arriving by direct-to-LDS loads one tile
 // ahead.  Per 32-query block:
 //   S  = Q K^T,  dP = dO V^T          A = Q / dO row fragments (LDS),
-//                                      B = K^T / V^T (registers, or LDS if KV_LDS)
+//                                      B = K^T / V^T (registers, or LDS: KVL)
 //   P, dS                              elementwise, in registers
 //   dV^T += dO^T P,  dK^T += Q^T dS    A = transposed LDS reads, B = P / dS
 // ATOMIC (the 5-GEMM design): each wave also writes its dS^T block to LDS; after a
 // barrier the workgroup computes dQ_tile = dS K over all BK keys (waves split the
 // (query block, d block) pairs) and adds it to dq with fp32 atomics, one atomic
 // per dq element per workgroup and query tile.
-// KV_LDS keeps the workgroup's K and V in LDS instead of registers (large d).
+// KVL: 0 keeps each wave's K and V fragments in registers; 1 reads both from the
+// workgroup's K and V tiles in LDS (large d); 2 (atomic shapes) reads K from the LDS
+// tile the dQ product needs anyway and keeps only V in registers.
 // D: LDS tile width (64, 128, 256); DV <= D (a multiple of 32): the head-dim columns
 // computed (96 and 192 run on 128- and 256-wide tiles without the zero columns' products).
-template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DROP>
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, int KVL, bool DROP>
 struct DkdvMath {
-  // K tile: plain row fragments (KV_LDS) and/or transposed reads (atomic dQ product)
-  static constexpr int KMODE = ATOMIC ? (KV_LDS ? kBoth : kColOnly) : kRowOnly;
+  static constexpr bool K_LDS = KVL != 0;
+  static constexpr bool V_LDS = KVL == 1;
+  // K tile: plain row fragments (K_LDS) and/or transposed reads (atomic dQ product)
+  static constexpr int KMODE = ATOMIC ? (K_LDS ? kBoth : kColOnly) : kRowOnly;
   static constexpr int BK = 32 * NW;
   static constexpr int QBN = BQ / 32;
   static constexpr int DB = DV / 32;
@@ -160,11 +164,14 @@ struct DkdvMath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           bf16x8 kb, vb;
-          if constexpr (KV_LDS) {
+          if constexpr (K_LDS) {
             kb = pk.row(ktile, wave * 32, kk);
-            vb = pv.row(vtile, wave * 32, kk);
           } else {
             kb = kf[kk];
+          }
+          if constexpr (V_LDS) {
+            vb = pv.row(vtile, wave * 32, kk);
+          } else {
             vb = vf[kk];
           }
           sc = mfma32(fr.row(qtl, 0, kk), kb, sc);
@@ -193,11 +200,14 @@ struct DkdvMath {
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
               bf16x8 kb, vb;
-              if constexpr (KV_LDS) {
+              if constexpr (K_LDS) {
                 kb = pk.row(ktile, wave * 32, kk);
-                vb = pv.row(vtile, wave * 32, kk);
               } else {
                 kb = kf[kk];
+              }
+              if constexpr (V_LDS) {
+                vb = pv.row(vtile, wave * 32, kk);
+              } else {
                 vb = vf[kk];
               }
               sn = mfma32(fr.row(qtl, (qb + 1) * 32, kk), kb, sn);
@@ -281,11 +291,14 @@ struct DkdvMath {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           bf16x8 kb, vb;
-          if constexpr (KV_LDS) {
+          if constexpr (K_LDS) {
             kb = pk.row(ktile, wave * 32, kk);
-            vb = pv.row(vtile, wave * 32, kk);
           } else {
             kb = kf[kk];
+          }
+          if constexpr (V_LDS) {
+            vb = pv.row(vtile, wave * 32, kk);
+          } else {
             vb = vf[kk];
           }
           s = mfma32(fr.row(qtl, qb * 32, kk), kb, s);
@@ -295,7 +308,7 @@ struct DkdvMath {
         // Interleave: fragment reads run two k-steps ahead of their MFMAs, so LDS
         // latency hides under the previous products instead of stalling the wave.
         if constexpr (kReadAhead) {
-          constexpr int RPS = KV_LDS ? 4 : 2;  // row-fragment reads per k-step
+          constexpr int RPS = 2 + K_LDS + V_LDS;  // row-fragment reads per k-step
           __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
 #pragma unroll
           for (int kk = 0; kk < KK - 2; ++kk) {
@@ -413,14 +426,15 @@ struct DkdvMath {
 
 // DEFER (atomic only): the dQ product and atomics of a query tile run at the start
 // of the next tile, from a second dS^T buffer, instead of behind an extra barrier.
-template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, bool KV_LDS, bool DEFER, bool DROP>
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC, int KVL, bool DEFER, bool DROP>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
-  using M = DkdvMath<D, DV, BQ, NW, CAUSAL, ATOMIC, KV_LDS, DROP>;
+  using M = DkdvMath<D, DV, BQ, NW, CAUSAL, ATOMIC, KVL, DROP>;
   constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
+  constexpr bool K_LDS = M::K_LDS, V_LDS = M::V_LDS;
   constexpr int NT = NW * 64;
   constexpr int QTILE = BQ * D * 2;
-  constexpr int KT_BYTES = (ATOMIC || KV_LDS) ? BK * D * 2 : 16;
-  constexpr int VT_BYTES = KV_LDS ? BK * D * 2 : 16;
+  constexpr int KT_BYTES = (ATOMIC || K_LDS) ? BK * D * 2 : 16;
+  constexpr int VT_BYTES = V_LDS ? BK * D * 2 : 16;
   constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 16;
   __shared__ __attribute__((aligned(1024))) char q0s[QTILE];
   __shared__ __attribute__((aligned(1024))) char d0s[QTILE];
@@ -482,12 +496,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   qdma.init(wave, lane, a.vq.sn, hd);
   qdma.issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
   qdma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
-  if constexpr (ATOMIC || KV_LDS) {
+  if constexpr (ATOMIC || K_LDS) {
     TileDMA<BK, D, NW, KMODE> kd;
     kd.init(wave, lane, a.vk.sn, hd);
     kd.issue(Kh, k0, N, ktile, wave, lane);
   }
-  if constexpr (KV_LDS) {
+  if constexpr (V_LDS) {
     TileDMA<BK, D, NW, kRowOnly> vd;
     vd.init(wave, lane, a.vv.sn, hd);
     vd.issue(Vh, k0, N, vtile, wave, lane);
@@ -496,13 +510,13 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   srow.load(lseh, delh, qt0 * BQ, N, tid);
   srow.store(st0, N, tid);
 
-  bf16x8 kf[KV_LDS ? 1 : KK], vf[KV_LDS ? 1 : KK];
-  if constexpr (!KV_LDS) {
+  bf16x8 kf[K_LDS ? 1 : KK], vf[V_LDS ? 1 : KK];
+  {
     const int krow_g = min(key, N - 1);  // keys past the end are masked (P = 0) and never stored
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      kf[kk] = load_row_chunk(Kh + (size_t)krow_g * a.vk.sn, 2 * kk + g, hd >> 3);
-      vf[kk] = load_row_chunk(Vh + (size_t)krow_g * a.vv.sn, 2 * kk + g, hd >> 3);
+      if constexpr (!K_LDS) kf[kk] = load_row_chunk(Kh + (size_t)krow_g * a.vk.sn, 2 * kk + g, hd >> 3);
+      if constexpr (!V_LDS) vf[kk] = load_row_chunk(Vh + (size_t)krow_g * a.vv.sn, 2 * kk + g, hd >> 3);
     }
   }
   f32x16 dk[DB], dv[DB];
@@ -517,20 +531,16 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
   fc.init(lane);
   RowOffsets<D, KMODE> pk;
   RowOffsets<D, kRowOnly> pv;
-  if constexpr (KV_LDS) {
-    pk.init(lane, true);
-    pv.init(lane, true);
-  }
+  if constexpr (K_LDS) pk.init(lane, true);
+  if constexpr (V_LDS) pv.init(lane, true);
 
   wait_tile();
   __syncthreads();
   for (int it = qt0; it < nqt; it += 2) {
     fr.refresh();
     fc.refresh();
-    if constexpr (KV_LDS) {
-      pk.refresh();
-      pv.refresh();
-    }
+    if constexpr (K_LDS) pk.refresh();
+    if constexpr (V_LDS) pv.refresh();
     qdma.refresh();
     if (it + 1 < nqt) {
       qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
@@ -552,10 +562,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
     if (it + 1 >= nqt) break;
     fr.refresh();
     fc.refresh();
-    if constexpr (KV_LDS) {
-      pk.refresh();
-      pv.refresh();
-    }
+    if constexpr (K_LDS) pk.refresh();
+    if constexpr (V_LDS) pv.refresh();
     qdma.refresh();
     if (it + 2 < nqt) {
       qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
@@ -777,7 +785,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D, int DV, int BQ, int NW, bool ATOMIC, bool KV_LDS, bool DEFER = false, bool DROP = false>
+template <int D, int DV, int BQ, int NW, bool ATOMIC, int KVL, bool DEFER = false, bool DROP = false>
 static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 32 * NW;
   const int nkt = (a.N + BK - 1) / BK;
@@ -785,10 +793,10 @@ static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, true, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, true, ATOMIC, KVL, DEFER, DROP>), dim3((unsigned)blocks),
                        dim3(NW * 64), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, false, ATOMIC, KV_LDS, DEFER, DROP>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((dkdv_kernel<D, DV, BQ, NW, false, ATOMIC, KVL, DEFER, DROP>), dim3((unsigned)blocks),
                        dim3(NW * 64), 0, stream, a);
   }
   return 0;
@@ -821,6 +829,24 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   {                                                                                                        \
     D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " deferred",         \
         &launch_dkdv<D, D, BQ, NW, true, KVL, true>                                                        \
+  }
+// K read from the LDS tile of the dQ product, V in registers (KVL = 2)
+#define DKDVADK_CFG(D, BQ, NW)                                                                           \
+  {                                                                                                        \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " k_lds deferred",                 \
+        &launch_dkdv<D, D, BQ, NW, true, 2, true>                                                          \
+  }
+#define DKDVADK_CFGV(D, DV, BQ, NW)                                                                      \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " k_lds deferred", \
+        &launch_dkdv<D, DV, BQ, NW, true, 2, true>                                                         \
+  }
+#define DKDVK_CFG(D, BQ, NW) \
+  { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " k_lds", &launch_dkdv<D, D, BQ, NW, false, 2> }
+#define DKDVK_CFGV(D, DV, BQ, NW)                                                                        \
+  {                                                                                                        \
+    DV, 32 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " k_lds",                  \
+        &launch_dkdv<D, DV, BQ, NW, false, 2>                                                              \
   }
 #define DQ_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, D, BC, NW, OCC> }
@@ -862,7 +888,9 @@ const BwdConfig* dkdv_configs(int* count) {
       DKDV_CFG(128, 64, 4, false), DKDV_CFG(128, 32, 4, false), DKDV_CFG(128, 32, 4, true),
       DKDV_CFG(128, 64, 4, true),  DKDV_CFG(128, 32, 2, true),
       DKDV_CFG(256, 32, 2, true),
+      DKDVK_CFG(128, 64, 4), DKDVK_CFG(256, 32, 4),
       DKDV_CFGV(128, 96, 64, 4, false), DKDV_CFGV(128, 96, 64, 4, true), DKDV_CFGV(256, 192, 32, 2, true),
+      DKDVK_CFGV(128, 96, 64, 4), DKDVK_CFGV(256, 192, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -874,7 +902,9 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       DKDVAD_CFG(64, 64, 8, false),
       DKDVA_CFG(128, 64, 4, false), DKDVA_CFG(128, 32, 4, false), DKDVAD_CFG(128, 64, 4, false),
       DKDVA_CFG(256, 32, 2, true),
+      DKDVADK_CFG(64, 64, 8), DKDVADK_CFG(128, 32, 8), DKDVADK_CFG(256, 32, 4),
       DKDVA_CFGV(128, 96, 64, 4, false), DKDVA_CFGV(256, 192, 32, 2, true),
+      DKDVADK_CFGV(128, 96, 32, 8), DKDVADK_CFGV(256, 192, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
