@@ -924,8 +924,8 @@ const BwdConfig* dq_configs(int* count) {
 // Dropout: the non-causal default shape of each head dim.
 const BwdConfig* dkdv_dropout_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDV_DROP_CFG(64, 64, 64, 8, false),  DKDV_DROP_CFG(128, 128, 64, 4, false), DKDV_DROP_CFG(256, 256, 32, 2, true),
-      DKDV_DROP_CFG(128, 96, 64, 4, false), DKDV_DROP_CFG(256, 192, 32, 2, true),
+      DKDV_DROP_CFG(64, 64, 64, 8, false), DKDV_DROP_CFG(128, 128, 64, 4, false), DKDV_DROP_CFG(256, 256, 32, 4, 2),
+      DKDV_DROP_CFG(128, 96, 64, 4, 2),    DKDV_DROP_CFG(256, 192, 32, 4, 2),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -933,9 +933,9 @@ const BwdConfig* dkdv_dropout_configs(int* count) {
 
 const BwdConfig* dkdv_atomic_dropout_configs(int* count) {
   static const BwdConfig table[] = {
-      DKDVA_DROP_CFG(64, 64, 64, 4, false, false),  DKDVA_DROP_CFG(128, 128, 64, 4, false, false),
-      DKDVA_DROP_CFG(256, 256, 32, 2, true, false), DKDVA_DROP_CFG(128, 96, 64, 4, false, false),
-      DKDVA_DROP_CFG(256, 192, 32, 2, true, false),
+      DKDVA_DROP_CFG(64, 64, 64, 8, 2, true),  DKDVA_DROP_CFG(128, 128, 32, 8, 2, true),
+      DKDVA_DROP_CFG(256, 256, 32, 4, 2, true), DKDVA_DROP_CFG(128, 96, 32, 8, 2, true),
+      DKDVA_DROP_CFG(256, 192, 32, 4, 2, true),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
