@@ -609,6 +609,346 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide dK/dV kernel (both designs): each wave owns two 32-key blocks (64 keys), so
+// every Q / dO row fragment and every transposed dO^T / Q^T fragment it reads from
+// LDS feeds two MFMAs, one per key block (the kernel above feeds one).  The dK^T and
+// dV^T accumulators of both blocks (4 D/32 fp32 x16 per lane) fill the accumulation
+// registers at d = 128, so one wave runs per SIMD.  K comes from the workgroup's K
+// tile in LDS (row fragments), V from registers.  Per 32-query block:
+//   S_b = Q K_b^T,  dP_b = dO V_b^T       (b = 0, 1; Q / dO fragments shared)
+//   P_b, dS_b                              elementwise, in registers
+//   dV_b^T += dO^T P_b,  dK_b^T += Q^T dS_b  (dO^T / Q^T fragments shared)
+// ATOMIC (the 5-GEMM design): each wave also writes its dS^T blocks to LDS, and at
+// the start of the next query tile the workgroup computes dQ_tile = dS K over its
+// BK = 64 NW keys (K by transposed reads of the same K tile) and adds it to dq with
+// one fp32 atomic per dq element, as the kernel above does with its deferred form.
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC>
+struct DkdvWideMath {
+  static constexpr int BK = 64 * NW;
+  static constexpr int QBN = BQ / 32;
+  static constexpr int DB = D / 32;
+  static constexpr int KK = D / 16;
+  // the K tile serves row fragments (S) and, for the dQ product, transposed reads
+  static constexpr int KMODE = ATOMIC ? kBoth : kRowOnly;
+
+  __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
+                                              const LDS char* ktile, LDS char* dst, const bf16x8 (&vf)[2][KK],
+                                              f32x16 (&dk)[2][DB], f32x16 (&dv)[2][DB], int q0, int kw, int key,
+                                              int N, float c, const RowOffsets<D, kBoth>& fr,
+                                              const ColOffsets<D, kBoth>& fc, const RowOffsets<D, KMODE>& pk,
+                                              int wave, int g, int l32) {
+    const LDS float* l2t = stats;
+    const LDS float* dlt = stats + BQ;
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+      const int qbase = q0 + qb * 32;
+      __builtin_amdgcn_sched_barrier(0);
+      // blocks past the end (P = 0), or above the causal diagonal for all 64 keys,
+      // contribute nothing; a block above the diagonal for the second key block
+      // only is computed with P = 0 there
+      if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          s[b] = zero16();
+          dp[b] = zero16();
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 qa = fr.row(qtl, qb * 32, kk);
+          const bf16x8 da = fr.row(dotl, qb * 32, kk);
+          const bf16x8 k0f = pk.row(ktile, wave * 64, kk);
+          const bf16x8 k1f = pk.row(ktile, wave * 64 + 32, kk);
+          s[0] = mfma32(qa, k0f, s[0]);
+          s[1] = mfma32(qa, k1f, s[1]);
+          dp[0] = mfma32(da, vf[0][kk], dp[0]);
+          dp[1] = mfma32(da, vf[1][kk], dp[1]);
+        }
+        // fragment reads (four per k-step) run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK - 2; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
+        float l2[16], dl[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int r = qb * 32 + 16 * h + 8 * g + 4 * hf;
+            const f32x4 lv = *(const LDS f32x4*)(l2t + r);
+            const f32x4 dd = *(const LDS f32x4*)(dlt + r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              l2[8 * h + 4 * hf + e] = lv[e];
+              dl[8 * h + 4 * hf + e] = dd[e];
+            }
+          }
+        }
+        // Queries past the end have lse2 = +inf (P = 0); keys past the end feed only
+        // their own dK/dV columns, which are never stored.
+        bf16x8 pb[2][2], sb[2][2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int kb = key + 32 * b;
+          const bool need_mask = CAUSAL && qbase < kw + 32 * b + 31;
+          f32x16 p, ds;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float pv = exp2_hw(fmaf(s[b][r], c, -l2[r]));
+            if (need_mask) {
+              const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
+              if (kb > q) pv = 0.f;
+            }
+            p[r] = pv;
+            ds[r] = pv * (dp[b][r] - dl[r]);
+          }
+          pb[b][0] = pack8(p, 0);
+          pb[b][1] = pack8(p, 8);
+          sb[b][0] = pack8(ds, 0);
+          sb[b][1] = pack8(ds, 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 o0 = fc.col(dotl, qb * 32, db);
+          const bf16x8 o1 = fc.col(dotl, qb * 32 + 16, db);
+          const bf16x8 t0 = fc.col(qtl, qb * 32, db);
+          const bf16x8 t1 = fc.col(qtl, qb * 32 + 16, db);
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            dv[b][db] = mfma32(o0, pb[b][0], dv[b][db]);
+            dv[b][db] = mfma32(o1, pb[b][1], dv[b][db]);
+            dk[b][db] = mfma32(t0, sb[b][0], dk[b][db]);
+            dk[b][db] = mfma32(t1, sb[b][1], dk[b][db]);
+          }
+        }
+        // transposed reads (8 per d block) run one d block ahead of their 8 MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int db = 0; db < DB - 1; ++db) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        if constexpr (ATOMIC) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            // keys past the end: K rows there are clamped copies, so their dS must not reach dQ
+            // (under the causal mask they are above the diagonal, dS = 0 already)
+            if (!CAUSAL && key + 32 * b >= N) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                sb[b][0][e] = (__bf16)0.f;
+                sb[b][1][e] = (__bf16)0.f;
+              }
+            }
+            const int krow = wave * 64 + 32 * b + l32;
+            *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(krow, qb * 32 + 8 * g)) = sb[b][0];
+            *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(krow, qb * 32 + 16 + 8 * g)) = sb[b][1];
+          }
+        }
+      } else if constexpr (ATOMIC) {
+        bf16x8 z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int krow = wave * 64 + 32 * b + l32;
+          *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(krow, qb * 32 + 8 * g)) = z;
+          *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(krow, qb * 32 + 16 + 8 * g)) = z;
+        }
+      }
+    }
+  }
+
+  // dQ_tile = dS K over the workgroup's BK keys (its dS^T blocks in LDS, written by
+  // tile() of the previous query tile and made visible by the barrier that ended it),
+  // one fp32 atomic per dq element; the waves split the (query block, d block) pairs.
+  __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
+                                                   int N, float scale, int wave, int g, int l32, int lane) {
+    for (int t = wave; t < QBN * DB; t += NW) {
+      const int qb = t / DB, db = t % DB;
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
+                     ColOffsets<D, kBoth>::col_dyn(ktile, ks * 16, db, lane), acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
+      }
+    }
+  }
+};
+
+template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC>
+__global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
+  using M = DkdvWideMath<D, BQ, NW, CAUSAL, ATOMIC>;
+  constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
+  constexpr int KMODE = M::KMODE;
+  constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 16;
+  constexpr int NT = NW * 64;
+  constexpr int QTILE = BQ * D * 2;
+  __shared__ __attribute__((aligned(1024))) char q0s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char d0s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char q1s[QTILE];
+  __shared__ __attribute__((aligned(1024))) char d1s[QTILE];
+  __shared__ __attribute__((aligned(16))) float st0s[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float st1s[2 * BQ];
+  __shared__ __attribute__((aligned(1024))) char kts[BK * D * 2];
+  // dS^T of alternate query tiles (the dQ product runs one tile late)
+  __shared__ __attribute__((aligned(1024))) char dsts0[DST_BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsts1[DST_BYTES];
+  LDS char* dst0 = (LDS char*)dsts0;
+  LDS char* dst1 = (LDS char*)dsts1;
+  LDS char* qbuf0 = (LDS char*)q0s;
+  LDS char* dbuf0 = (LDS char*)d0s;
+  LDS char* qbuf1 = (LDS char*)q1s;
+  LDS char* dbuf1 = (LDS char*)d1s;
+  LDS float* st0 = (LDS float*)st0s;
+  LDS float* st1 = (LDS float*)st1s;
+  LDS char* ktile = (LDS char*)kts;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int N = a.N;
+  const int nkt = (N + BK - 1) / BK;
+  int bh, kt;
+  if (CAUSAL) {
+    causal_order(blockIdx.x, a.B * a.H, nkt, false, bh, kt);  // low key tiles see the most queries
+  } else {
+    const int item = xcd_remap(blockIdx.x, a.B * a.H * nkt);
+    bh = item / nkt;
+    kt = item % nkt;
+  }
+  const __bf16* Qh = a.q + head_base(a.vq, bh, a.H);
+  const __bf16* Kh = a.k + head_base(a.vk, bh, a.H);
+  const __bf16* Vh = a.v + head_base(a.vv, bh, a.H);
+  const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
+  const float* lseh = a.lse + (size_t)bh * N;
+  const float* delh = a.delta + (size_t)bh * N;
+  // the atomic dq is a contiguous [B, H, N, D] accumulator (columns past the head dim
+  // receive zeros, since K is zero there)
+  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * D : nullptr;
+  const int hd = a.hd;  // columns hd .. D-1 are zero padding
+  const float c = a.scale * kLog2e;
+
+  const int k0 = kt * BK;
+  const int kw = k0 + wave * 64;  // the wave's keys: kw + l32 (block 0), kw + 32 + l32 (block 1)
+  const int key = kw + l32;
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  // Q, dO: row fragments and transposed reads; one copier serves both (equal row pitches)
+  TileDMA<BQ, D, NW, kBoth> qdma;
+  qdma.init(wave, lane, a.vq.sn, hd);
+  qdma.issue(Qh, qt0 * BQ, N, qbuf0, wave, lane);
+  qdma.issue(dOh, qt0 * BQ, N, dbuf0, wave, lane);
+  {
+    TileDMA<BK, D, NW, KMODE> kd;
+    kd.init(wave, lane, a.vk.sn, hd);
+    kd.issue(Kh, k0, N, ktile, wave, lane);
+  }
+  RowStager<BQ, NT> srow;
+  srow.load(lseh, delh, qt0 * BQ, N, tid);
+  srow.store(st0, N, tid);
+
+  bf16x8 vf[2][KK];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int vrow = min(key + 32 * b, N - 1);  // keys past the end are never stored
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) vf[b][kk] = load_row_chunk(Vh + (size_t)vrow * a.vv.sn, 2 * kk + g, hd >> 3);
+  }
+  f32x16 dk[2][DB], dv[2][DB];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      dk[b][db] = zero16();
+      dv[b][db] = zero16();
+    }
+  }
+  RowOffsets<D, kBoth> fr;
+  fr.init(lane);
+  ColOffsets<D, kBoth> fc;
+  fc.init(lane);
+  RowOffsets<D, KMODE> pk;
+  pk.init(lane, true);
+
+  wait_tile();
+  __syncthreads();
+  for (int it = qt0; it < nqt; it += 2) {
+    fr.refresh();
+    fc.refresh();
+    pk.refresh();
+    qdma.refresh();
+    if (it + 1 < nqt) {
+      qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
+      qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
+      srow.load(lseh, delh, (it + 1) * BQ, N, tid);
+    }
+    if constexpr (ATOMIC) {
+      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
+    }
+    M::tile(qbuf0, dbuf0, st0, ktile, dst0, vf, dk, dv, it * BQ, kw, key, N, c, fr, fc, pk, wave, g, l32);
+    wait_tile();
+    if (it + 1 < nqt) srow.store(st1, N, tid);
+    __syncthreads();
+    if (it + 1 >= nqt) break;
+    fr.refresh();
+    fc.refresh();
+    pk.refresh();
+    qdma.refresh();
+    if (it + 2 < nqt) {
+      qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
+      qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
+      srow.load(lseh, delh, (it + 2) * BQ, N, tid);
+    }
+    if constexpr (ATOMIC) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
+    M::tile(qbuf1, dbuf1, st1, ktile, dst1, vf, dk, dv, (it + 1) * BQ, kw, key, N, c, fr, fc, pk, wave, g, l32);
+    wait_tile();
+    if (it + 2 < nqt) srow.store(st0, N, tid);
+    __syncthreads();
+  }
+  if constexpr (ATOMIC) {  // dQ of the last query tile (its dS^T buffer alternates with the tile's parity)
+    const int last = nqt - 1;
+    M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane);
+  }
+
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int kb = key + 32 * b;
+    if (kb < N) {
+      float* dkr = a.dk + head_base(a.vdk, bh, a.H) + (size_t)kb * a.vdk.sn;
+      float* dvr = a.dv + head_base(a.vdv, bh, a.H) + (size_t)kb * a.vdv.sn;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int col = db * 32 + 8 * a4 + 4 * g;
+          const f32x4 kv = {dk[b][db][4 * a4] * a.scale, dk[b][db][4 * a4 + 1] * a.scale,
+                            dk[b][db][4 * a4 + 2] * a.scale, dk[b][db][4 * a4 + 3] * a.scale};
+          const f32x4 vv = {dv[b][db][4 * a4], dv[b][db][4 * a4 + 1], dv[b][db][4 * a4 + 2],
+                            dv[b][db][4 * a4 + 3]};
+          if (col < hd) {
+            *(f32x4*)(dkr + col) = kv;
+            *(f32x4*)(dvr + col) = vv;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dQ kernel of the 7-GEMM design: one workgroup owns BR = 32 * NW queries, each
 // wave 32 (one per lane column), and walks the key/value tiles in the forward's
 // direction, the tiles arriving by direct-to-LDS loads one tile ahead.  Per tile:
@@ -802,6 +1142,23 @@ static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   return 0;
 }
 
+template <int D, int BQ, int NW, bool ATOMIC>
+static int launch_dkdv_wide(const BwdArgs& a, bool causal, hipStream_t stream) {
+  constexpr int BK = 64 * NW;
+  const int nkt = (a.N + BK - 1) / BK;
+  const long long blocks = (long long)a.B * a.H * nkt;
+  if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+  if (a.drop_t != 0) return -1;
+  if (causal) {
+    hipLaunchKernelGGL((dkdv_wide_kernel<D, BQ, NW, true, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
+  } else {
+    hipLaunchKernelGGL((dkdv_wide_kernel<D, BQ, NW, false, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+                       a);
+  }
+  return 0;
+}
+
 template <int D, int DV, int BC, int NW, int OCC, bool DROP = false>
 static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
@@ -848,6 +1205,14 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
     DV, 32 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " k_lds",                  \
         &launch_dkdv<D, DV, BQ, NW, false, 2>                                                              \
   }
+// two 32-key blocks per wave (dkdv_wide_kernel), K read from LDS
+#define DKDVW_CFG(D, BQ, NW) \
+  { D, 64 * (NW), BQ, NW, "dkdv d" #D " Bk64x" #NW " Bq" #BQ " k_lds wide", &launch_dkdv_wide<D, BQ, NW, false> }
+#define DKDVAW_CFG(D, BQ, NW)                                                                             \
+  {                                                                                                        \
+    D, 64 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk64x" #NW " Bq" #BQ " k_lds deferred wide",            \
+        &launch_dkdv_wide<D, BQ, NW, true>                                                                 \
+  }
 #define DQ_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, D, BC, NW, OCC> }
 // head dim DV on D-wide tiles (the table's key is DV)
@@ -891,6 +1256,7 @@ const BwdConfig* dkdv_configs(int* count) {
       DKDVK_CFG(128, 64, 4), DKDVK_CFG(256, 32, 4),
       DKDV_CFGV(128, 96, 64, 4, false), DKDV_CFGV(128, 96, 64, 4, true), DKDV_CFGV(256, 192, 32, 2, true),
       DKDVK_CFGV(128, 96, 64, 4), DKDVK_CFGV(256, 192, 32, 4),
+      DKDVW_CFG(64, 64, 4),  DKDVW_CFG(64, 32, 4),  DKDVW_CFG(128, 64, 4), DKDVW_CFG(128, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -905,6 +1271,7 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       DKDVADK_CFG(64, 64, 8), DKDVADK_CFG(128, 32, 8), DKDVADK_CFG(256, 32, 4),
       DKDVA_CFGV(128, 96, 64, 4, false), DKDVA_CFGV(256, 192, 32, 2, true),
       DKDVADK_CFGV(128, 96, 32, 8), DKDVADK_CFGV(256, 192, 32, 4),
+      DKDVAW_CFG(64, 64, 4),  DKDVAW_CFG(64, 32, 4),  DKDVAW_CFG(128, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
