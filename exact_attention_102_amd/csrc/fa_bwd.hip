@@ -766,12 +766,25 @@ struct DkdvWideMath {
     }
   }
 
+  // When the (query block, d block) pairs split evenly over the waves, every wave
+  // issues exactly kAtomics atomic instructions per dQ product (rows past the end add
+  // 0 to the last row instead of being skipped), and the kernel issues one product
+  // per query tile, so the end-of-tile wait can leave them in flight: vmcnt retires
+  // in issue order, and the tile copies were issued before them.
+  static constexpr bool kEvenSplit = (QBN * DB) % NW == 0;
+  static constexpr int kPerWave = (QBN * DB + NW - 1) / NW;  // (qb, db) pairs per wave (at most)
+  static constexpr int kAtomics = 16 * kPerWave;
+  static_assert(!ATOMIC || !kEvenSplit || kAtomics < 64, "vmcnt holds at most 63");
+
   // dQ_tile = dS K over the workgroup's BK keys (its dS^T blocks in LDS, written by
   // tile() of the previous query tile and made visible by the barrier that ended it),
   // one fp32 atomic per dq element; the waves split the (query block, d block) pairs.
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
                                                    int N, float scale, int wave, int g, int l32, int lane) {
-    for (int t = wave; t < QBN * DB; t += NW) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int t = wave + i * NW;
+      if (!kEvenSplit && t >= QBN * DB) break;
       const int qb = t / DB, db = t % DB;
       f32x16 acc = zero16();
 #pragma unroll
@@ -782,9 +795,27 @@ struct DkdvWideMath {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (q < N) unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
+        if constexpr (kEvenSplit) {
+          unsafeAtomicAdd(dqh + (size_t)min(q, N - 1) * D + db * 32 + l32, q < N ? acc[r] * scale : 0.f);
+        } else if (q < N) {
+          unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
+        }
       }
     }
+  }
+
+  // End of a query tile: the tile copies issued at its start must have landed.  With
+  // `atomics` true the last kAtomics vector-memory instructions of this wave are the
+  // dQ atomics issued after those copies (and after the statistics load, which the
+  // compiler waits for itself), and they may stay outstanding.
+  __device__ __forceinline__ static void end_tile_wait(bool atomics) {
+    if constexpr (ATOMIC && kEvenSplit) {
+      if (atomics) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_wait(kAtomics));
+        return;
+      }
+    }
+    wait_tile();
   }
 };
 
@@ -882,6 +913,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
   fc.init(lane);
   RowOffsets<D, KMODE> pk;
   pk.init(lane, true);
+  if constexpr (ATOMIC && M::kEvenSplit) {
+    // the first query tile's dQ product reads this buffer before any tile wrote it:
+    // zeros, so that product adds 0 (it keeps every tile's atomic count equal)
+    bf16x8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.f;
+    for (int i = tid; i < DST_BYTES / 16; i += NT) *(LDS bf16x8*)(dst1 + 16 * i) = z;
+  }
 
   wait_tile();
   __syncthreads();
@@ -893,14 +932,21 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
     if (it + 1 < nqt) {
       qdma.issue(Qh, (it + 1) * BQ, N, qbuf1, wave, lane);
       qdma.issue(dOh, (it + 1) * BQ, N, dbuf1, wave, lane);
-      srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     }
+    // ATOMIC: the statistics load and store run on every path (past the last tile they
+    // read a clamped row and fill the unused buffer), so the compiler's own wait for the
+    // load can count the atomics issued after it instead of waiting for them
+    if (ATOMIC || it + 1 < nqt) srow.load(lseh, delh, (it + 1) * BQ, N, tid);
     if constexpr (ATOMIC) {
-      if (it > qt0) M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
+      if constexpr (M::kEvenSplit) {  // at the first tile: the zeroed buffer, added to valid rows
+        M::atomic_dq(dst1, ktile, dqh, (it > qt0 ? it - 1 : it) * BQ, N, a.scale, wave, g, l32, lane);
+      } else if (it > qt0) {
+        M::atomic_dq(dst1, ktile, dqh, (it - 1) * BQ, N, a.scale, wave, g, l32, lane);
+      }
     }
     M::tile(qbuf0, dbuf0, st0, ktile, dst0, vf, dk, dv, it * BQ, kw, key, N, c, fr, fc, pk, wave, g, l32);
-    wait_tile();
-    if (it + 1 < nqt) srow.store(st1, N, tid);
+    M::end_tile_wait(ATOMIC);
+    if (ATOMIC || it + 1 < nqt) srow.store(st1, N, tid);
     __syncthreads();
     if (it + 1 >= nqt) break;
     fr.refresh();
@@ -910,12 +956,12 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
     if (it + 2 < nqt) {
       qdma.issue(Qh, (it + 2) * BQ, N, qbuf0, wave, lane);
       qdma.issue(dOh, (it + 2) * BQ, N, dbuf0, wave, lane);
-      srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     }
+    if (ATOMIC || it + 2 < nqt) srow.load(lseh, delh, (it + 2) * BQ, N, tid);
     if constexpr (ATOMIC) M::atomic_dq(dst0, ktile, dqh, it * BQ, N, a.scale, wave, g, l32, lane);
     M::tile(qbuf1, dbuf1, st1, ktile, dst1, vf, dk, dv, (it + 1) * BQ, kw, key, N, c, fr, fc, pk, wave, g, l32);
-    wait_tile();
-    if (it + 2 < nqt) srow.store(st0, N, tid);
+    M::end_tile_wait(ATOMIC);
+    if (ATOMIC || it + 2 < nqt) srow.store(st0, N, tid);
     __syncthreads();
   }
   if constexpr (ATOMIC) {  // dQ of the last query tile (its dS^T buffer alternates with the tile's parity)
