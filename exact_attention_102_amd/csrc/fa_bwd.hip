@@ -647,46 +647,38 @@ struct DkdvWideMath {
       // contribute nothing; a block above the diagonal for the second key block
       // only is computed with P = 0 there
       if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
-        f32x16 s[2], dp[2];
+        // S of both key blocks first (Q fragments shared), then P; then dP (dO fragments
+        // shared) and dS.  Only one of S and dP is live at a time, which keeps both out
+        // of the accumulation registers the dK/dV accumulators fill.
+        f32x16 p[2];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          s[b] = zero16();
-          dp[b] = zero16();
-        }
+        for (int b = 0; b < 2; ++b) p[b] = zero16();
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const bf16x8 qa = fr.row(qtl, qb * 32, kk);
-          const bf16x8 da = fr.row(dotl, qb * 32, kk);
           const bf16x8 k0f = pk.row(ktile, wave * 64, kk);
           const bf16x8 k1f = pk.row(ktile, wave * 64 + 32, kk);
-          s[0] = mfma32(qa, k0f, s[0]);
-          s[1] = mfma32(qa, k1f, s[1]);
-          dp[0] = mfma32(da, vf[0][kk], dp[0]);
-          dp[1] = mfma32(da, vf[1][kk], dp[1]);
+          p[0] = mfma32(qa, k0f, p[0]);
+          p[1] = mfma32(qa, k1f, p[1]);
         }
-        // fragment reads (four per k-step) run two k-steps ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // fragment reads (three per k-step) run two k-steps ahead of their MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int kk = 0; kk < KK - 2; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         __builtin_amdgcn_sched_barrier(0);
         // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
-        float l2[16], dl[16];
+        float l2[16];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const int r = qb * 32 + 16 * h + 8 * g + 4 * hf;
-            const f32x4 lv = *(const LDS f32x4*)(l2t + r);
-            const f32x4 dd = *(const LDS f32x4*)(dlt + r);
+            const f32x4 lv = *(const LDS f32x4*)(l2t + qb * 32 + 16 * h + 8 * g + 4 * hf);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              l2[8 * h + 4 * hf + e] = lv[e];
-              dl[8 * h + 4 * hf + e] = dd[e];
-            }
+            for (int e = 0; e < 4; ++e) l2[8 * h + 4 * hf + e] = lv[e];
           }
         }
         // Queries past the end have lse2 = +inf (P = 0); keys past the end feed only
@@ -696,19 +688,52 @@ struct DkdvWideMath {
         for (int b = 0; b < 2; ++b) {
           const int kb = key + 32 * b;
           const bool need_mask = CAUSAL && qbase < kw + 32 * b + 31;
-          f32x16 p, ds;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float pv = exp2_hw(fmaf(s[b][r], c, -l2[r]));
+            float pv = exp2_hw(fmaf(p[b][r], c, -l2[r]));
             if (need_mask) {
               const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
               if (kb > q) pv = 0.f;
             }
-            p[r] = pv;
-            ds[r] = pv * (dp[b][r] - dl[r]);
+            p[b][r] = pv;
           }
-          pb[b][0] = pack8(p, 0);
-          pb[b][1] = pack8(p, 8);
+          pb[b][0] = pack8(p[b], 0);
+          pb[b][1] = pack8(p[b], 8);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16 dp[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) dp[b] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const bf16x8 da = fr.row(dotl, qb * 32, kk);
+          dp[0] = mfma32(da, vf[0][kk], dp[0]);
+          dp[1] = mfma32(da, vf[1][kk], dp[1]);
+        }
+        // dO fragment reads run two k-steps ahead
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+        for (int kk = 0; kk < KK - 2; ++kk) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        float dl[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const f32x4 dd = *(const LDS f32x4*)(dlt + qb * 32 + 16 * h + 8 * g + 4 * hf);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dl[8 * h + 4 * hf + e] = dd[e];
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          f32x16 ds;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] = p[b][r] * (dp[b][r] - dl[r]);
           sb[b][0] = pack8(ds, 0);
           sb[b][1] = pack8(ds, 8);
         }
