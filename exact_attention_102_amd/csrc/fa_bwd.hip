@@ -792,10 +792,11 @@ struct DkdvWideMath {
   }
 
   // When the (query block, d block) pairs split evenly over the waves, every wave
-  // issues exactly kAtomics atomic instructions per dQ product (rows past the end add
-  // 0 to the last row instead of being skipped), and the kernel issues one product
-  // per query tile, so the end-of-tile wait can leave them in flight: vmcnt retires
-  // in issue order, and the tile copies were issued before them.
+  // issues exactly kAtomics atomic instructions per dQ product (none is skipped: rows
+  // past the end fall outside the buffer range below and the hardware drops them),
+  // and the kernel issues one product per query tile, so the end-of-tile wait can
+  // leave them in flight: vmcnt retires in issue order, and the tile copies were
+  // issued before them.
   static constexpr bool kEvenSplit = (QBN * DB) % NW == 0;
   static constexpr int kPerWave = (QBN * DB + NW - 1) / NW;  // (qb, db) pairs per wave (at most)
   static constexpr int kAtomics = 16 * kPerWave;
@@ -804,8 +805,14 @@ struct DkdvWideMath {
   // dQ_tile = dS K over the workgroup's BK keys (its dS^T blocks in LDS, written by
   // tile() of the previous query tile and made visible by the barrier that ended it),
   // one fp32 atomic per dq element; the waves split the (query block, d block) pairs.
+  // The adds are buffer atomics over the head's N x D accumulator: one 32-bit lane
+  // offset per pair, the per-register row steps in the scalar and immediate offsets,
+  // and rows past the end beyond the buffer range (N * D * 4 + 32 rows fit 32 bits;
+  // the launcher checks).
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
                                                    int N, float scale, int wave, int g, int l32, int lane) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(dqh, (short)0, (int)((unsigned)N * (unsigned)(D * 4)), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int t = wave + i * NW;
@@ -817,15 +824,12 @@ struct DkdvWideMath {
         acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
                      ColOffsets<D, kBoth>::col_dyn(ktile, ks * 16, db, lane), acc);
       }
+      // register r holds row q0 + 32 qb + 4 g + 8 (r / 4) + r % 4, column 32 db + l32
+      const unsigned off = ((unsigned)(q0 + qb * 32 + 4 * g) * D + db * 32 + l32) * 4u;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if constexpr (kEvenSplit) {
-          unsafeAtomicAdd(dqh + (size_t)min(q, N - 1) * D + db * 32 + l32, q < N ? acc[r] * scale : 0.f);
-        } else if (q < N) {
-          unsafeAtomicAdd(dqh + (size_t)q * D + db * 32 + l32, acc[r] * scale);
-        }
-      }
+      for (int r = 0; r < 16; ++r)
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rs, off + (r & 3) * (D * 4),
+                                                        8 * (r >> 2) * (D * 4), 0);
     }
   }
 
@@ -1220,6 +1224,10 @@ static int launch_dkdv_wide(const BwdArgs& a, bool causal, hipStream_t stream) {
   const long long blocks = (long long)a.B * a.H * nkt;
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if (a.drop_t != 0) return -1;
+  // the atomic dQ product addresses a head's accumulator (plus 32 rows past its end)
+  // with 32-bit buffer offsets; heads beyond that take the 8-wave kernel
+  if (ATOMIC && ((long long)a.N + 32) * D * 4 > 0xffffffffLL)
+    return launch_dkdv<D, D, D == 64 ? 64 : 32, 8, true, 2, true>(a, causal, stream);
   if (causal) {
     hipLaunchKernelGGL((dkdv_wide_kernel<D, BQ, NW, true, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
