@@ -86,12 +86,12 @@ int default_index(int pass, int d, int causal) {
       if (d == 128) return 4;
       if (causal && d == 96) return 2;
       return d == 64 ? (causal ? 2 : 4) : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
-    case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d96 Bk32x4 Bq64, d192 and d256 Bk32x4 Bq32, K
-             // read from LDS; d128 two key blocks per wave, Bk64x4 Bq64
-      return d == 64 ? 2 : d == 96 ? 2 : d == 128 ? 6 : 1;
-    case 2:  // dkdv + atomic dq, K read from LDS, dQ one tile late: d64 Bk32x8 Bq64, d96 Bk32x8 Bq32, d192
-             // and d256 Bk32x4 Bq32; d128 two key blocks per wave, Bk64x4 Bq32
-      return d == 64 ? 4 : d == 128 ? 4 : 1;
+    case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d192 and d256 Bk32x4 Bq32, K read from LDS; d96
+             // and d128 two key blocks per wave, Bk64x4 Bq64
+      return d == 64 ? 2 : d == 96 ? 3 : d == 128 ? 6 : 1;
+    case 2:  // dkdv + atomic dq, K read from LDS, dQ one tile late: d64 Bk32x8 Bq64, causal d96 Bk32x8 Bq32,
+             // d192 and d256 Bk32x4 Bq32; d128 and non-causal d96 two key blocks per wave, Bk64x4 Bq32
+      return d == 64 ? 4 : d == 128 ? 4 : d == 96 ? (causal ? 1 : 2) : 1;
     case 3:                                           // dq: d128 non-causal Bq32x8 Bc64, d96 causal Bq32x8
       return ((d == 128 && !causal) ? 2 : 0) + ((d == 96 && causal) ? 1 : 0);
     default: return -1;

@@ -622,12 +622,14 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_kernel(BwdArgs a) {
 // the start of the next query tile the workgroup computes dQ_tile = dS K over its
 // BK = 64 NW keys (K by transposed reads of the same K tile) and adds it to dq with
 // one fp32 atomic per dq element, as the kernel above does with its deferred form.
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC>
+// D: LDS tile width; DV <= D (a multiple of 32): the head-dim columns computed (96 on
+// 128-wide tiles, where the accumulators take 192 of the 256 accumulation registers).
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC>
 struct DkdvWideMath {
   static constexpr int BK = 64 * NW;
   static constexpr int QBN = BQ / 32;
-  static constexpr int DB = D / 32;
-  static constexpr int KK = D / 16;
+  static constexpr int DB = DV / 32;
+  static constexpr int KK = DV / 16;
   // the K tile serves row fragments (S) and, for the dQ product, transposed reads
   static constexpr int KMODE = ATOMIC ? kBoth : kRowOnly;
 
@@ -807,12 +809,12 @@ struct DkdvWideMath {
   // one fp32 atomic per dq element; the waves split the (query block, d block) pairs.
   // The adds are buffer atomics over the head's N x D accumulator: one 32-bit lane
   // offset per pair, the per-register row steps in the scalar and immediate offsets,
-  // and rows past the end beyond the buffer range (N * D * 4 + 32 rows fit 32 bits;
+  // and rows past the end beyond the buffer range (N * DV * 4 + 32 rows fit 32 bits;
   // the launcher checks).
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
                                                    int N, float scale, int wave, int g, int l32, int lane) {
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(dqh, (short)0, (int)((unsigned)N * (unsigned)(D * 4)), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(dqh, (short)0, (int)((unsigned)N * (unsigned)(DV * 4)), 0x00020000);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i) {
       const int t = wave + i * NW;
@@ -825,11 +827,11 @@ struct DkdvWideMath {
                      ColOffsets<D, kBoth>::col_dyn(ktile, ks * 16, db, lane), acc);
       }
       // register r holds row q0 + 32 qb + 4 g + 8 (r / 4) + r % 4, column 32 db + l32
-      const unsigned off = ((unsigned)(q0 + qb * 32 + 4 * g) * D + db * 32 + l32) * 4u;
+      const unsigned off = ((unsigned)(q0 + qb * 32 + 4 * g) * DV + db * 32 + l32) * 4u;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rs, off + (r & 3) * (D * 4),
-                                                        8 * (r >> 2) * (D * 4), 0);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rs, off + (r & 3) * (DV * 4),
+                                                        8 * (r >> 2) * (DV * 4), 0);
     }
   }
 
@@ -848,9 +850,9 @@ struct DkdvWideMath {
   }
 };
 
-template <int D, int BQ, int NW, bool CAUSAL, bool ATOMIC>
+template <int D, int DV, int BQ, int NW, bool CAUSAL, bool ATOMIC>
 __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
-  using M = DkdvWideMath<D, BQ, NW, CAUSAL, ATOMIC>;
+  using M = DkdvWideMath<D, DV, BQ, NW, CAUSAL, ATOMIC>;
   constexpr int BK = M::BK, DB = M::DB, KK = M::KK;
   constexpr int KMODE = M::KMODE;
   constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 16;
@@ -895,9 +897,9 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
   const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
   const float* lseh = a.lse + (size_t)bh * N;
   const float* delh = a.delta + (size_t)bh * N;
-  // the atomic dq is a contiguous [B, H, N, D] accumulator (columns past the head dim
+  // the atomic dq is a contiguous [B, H, N, DV] accumulator (columns past the head dim
   // receive zeros, since K is zero there)
-  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * D : nullptr;
+  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * DV : nullptr;
   const int hd = a.hd;  // columns hd .. D-1 are zero padding
   const float c = a.scale * kLog2e;
 
@@ -1217,7 +1219,7 @@ static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   return 0;
 }
 
-template <int D, int BQ, int NW, bool ATOMIC>
+template <int D, int DV, int BQ, int NW, bool ATOMIC>
 static int launch_dkdv_wide(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 64 * NW;
   const int nkt = (a.N + BK - 1) / BK;
@@ -1226,13 +1228,13 @@ static int launch_dkdv_wide(const BwdArgs& a, bool causal, hipStream_t stream) {
   if (a.drop_t != 0) return -1;
   // the atomic dQ product addresses a head's accumulator (plus 32 rows past its end)
   // with 32-bit buffer offsets; heads beyond that take the 8-wave kernel
-  if (ATOMIC && ((long long)a.N + 32) * D * 4 > 0xffffffffLL)
-    return launch_dkdv<D, D, D == 64 ? 64 : 32, 8, true, 2, true>(a, causal, stream);
+  if (ATOMIC && ((long long)a.N + 32) * DV * 4 > 0xffffffffLL)
+    return launch_dkdv<D, DV, DV == 64 ? 64 : 32, 8, true, 2, true>(a, causal, stream);
   if (causal) {
-    hipLaunchKernelGGL((dkdv_wide_kernel<D, BQ, NW, true, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((dkdv_wide_kernel<D, DV, BQ, NW, true, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   } else {
-    hipLaunchKernelGGL((dkdv_wide_kernel<D, BQ, NW, false, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((dkdv_wide_kernel<D, DV, BQ, NW, false, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   }
   return 0;
@@ -1286,11 +1288,21 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   }
 // two 32-key blocks per wave (dkdv_wide_kernel), K read from LDS
 #define DKDVW_CFG(D, BQ, NW) \
-  { D, 64 * (NW), BQ, NW, "dkdv d" #D " Bk64x" #NW " Bq" #BQ " k_lds wide", &launch_dkdv_wide<D, BQ, NW, false> }
+  { D, 64 * (NW), BQ, NW, "dkdv d" #D " Bk64x" #NW " Bq" #BQ " k_lds wide", &launch_dkdv_wide<D, D, BQ, NW, false> }
 #define DKDVAW_CFG(D, BQ, NW)                                                                             \
   {                                                                                                        \
     D, 64 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk64x" #NW " Bq" #BQ " k_lds deferred wide",            \
-        &launch_dkdv_wide<D, BQ, NW, true>                                                                 \
+        &launch_dkdv_wide<D, D, BQ, NW, true>                                                              \
+  }
+#define DKDVW_CFGV(D, DV, BQ, NW)                                                                        \
+  {                                                                                                        \
+    DV, 64 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk64x" #NW " Bq" #BQ " k_lds wide",             \
+        &launch_dkdv_wide<D, DV, BQ, NW, false>                                                            \
+  }
+#define DKDVAW_CFGV(D, DV, BQ, NW)                                                                       \
+  {                                                                                                        \
+    DV, 64 * (NW), BQ, NW, "dkdv+atomic-dq d" #DV " (tiles " #D ") Bk64x" #NW " Bq" #BQ " k_lds deferred wide", \
+        &launch_dkdv_wide<D, DV, BQ, NW, true>                                                             \
   }
 #define DQ_CFG(D, BC, NW, OCC) \
   { D, 32 * (NW), BC, NW, "dq d" #D " Bq32x" #NW " Bc" #BC " occ" #OCC, &launch_dq<D, D, BC, NW, OCC> }
@@ -1336,6 +1348,7 @@ const BwdConfig* dkdv_configs(int* count) {
       DKDV_CFGV(128, 96, 64, 4, false), DKDV_CFGV(128, 96, 64, 4, true), DKDV_CFGV(256, 192, 32, 2, true),
       DKDVK_CFGV(128, 96, 64, 4), DKDVK_CFGV(256, 192, 32, 4),
       DKDVW_CFG(64, 64, 4),  DKDVW_CFG(64, 32, 4),  DKDVW_CFG(128, 64, 4), DKDVW_CFG(128, 32, 4),
+      DKDVW_CFGV(128, 96, 64, 4), DKDVW_CFGV(128, 96, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -1350,7 +1363,7 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       DKDVADK_CFG(64, 64, 8), DKDVADK_CFG(128, 32, 8), DKDVADK_CFG(256, 32, 4),
       DKDVA_CFGV(128, 96, 64, 4, false), DKDVA_CFGV(256, 192, 32, 2, true),
       DKDVADK_CFGV(128, 96, 32, 8), DKDVADK_CFGV(256, 192, 32, 4),
-      DKDVAW_CFG(64, 64, 4),  DKDVAW_CFG(64, 32, 4),  DKDVAW_CFG(128, 32, 4),
+      DKDVAW_CFG(64, 64, 4),  DKDVAW_CFG(64, 32, 4),  DKDVAW_CFG(128, 32, 4), DKDVAW_CFGV(128, 96, 32, 4),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -1,6 +1,6 @@
 """Block-shape sweep: times every tile configuration of every kernel on one workload.
 
-    python -m exact_attention_102_amd.sweep --workload b4_h16_n2048_d128 [--causal 0|1] [--out file.jsonl]
+    python -m exact_attention_102_amd.sweep --workload b4_h16_n2048_d128 [--causal 0|1] [--d 96] [--passes 0,1,2,3]
 
 "Potential algorithmic improvements for backward pass" (flash-attention issue 1172)
 treats the block shape -- rows owned per workgroup x rows walked per tile, and
@@ -14,6 +14,7 @@ these results.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -42,7 +43,7 @@ def time_calls(fn, torch, trials=5, dispatches=5, warmup=2):
     return per[0], per[len(per) // 2]
 
 
-def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3)):
+def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3), d_override: int = 0):
     import torch
 
     import workloads
@@ -51,6 +52,8 @@ def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3)):
     from exact_attention_102_amd.flops import attention_flops
 
     w = workloads.WORKLOADS[workload]
+    if d_override:  # same batch, heads, length and seed at another head dim
+        w = dataclasses.replace(w, name="%s_hd%d" % (w.name, d_override), d=d_override)
     causal = w.causal if causal_override is None else bool(causal_override)
     B, H, N, d = w.B, w.H, w.N, w.d
     q, k, v, do = (workloads.to_bf16(x).cuda() for x in workloads.draw_workload(w))
@@ -91,8 +94,10 @@ def main():
     ap.add_argument("--workload", default="b4_h16_n2048_d128")
     ap.add_argument("--causal", type=int, default=-1)
     ap.add_argument("--passes", default="0,1,2,3")
+    ap.add_argument("--d", type=int, default=0, help="head dim in place of the workload's")
     args = ap.parse_args()
-    sweep(args.workload, None if args.causal < 0 else args.causal, tuple(int(x) for x in args.passes.split(",")))
+    sweep(args.workload, None if args.causal < 0 else args.causal, tuple(int(x) for x in args.passes.split(",")),
+          args.d)
 
 
 if __name__ == "__main__":
