@@ -85,12 +85,12 @@ def classify(name: str):
         return None
     kind, targs = m.group(1), [t.strip() for t in m.group(2).split(",")]
     # template arguments: fwd / dq <D, DV, tile, waves, occupancy, CAUSAL, DROP>;
-    # dkdv <D, DV, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>; dkdv_wide <D, BQ, waves, CAUSAL, ATOMIC>;
+    # dkdv <D, DV, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>; dkdv_wide <D, DV, BQ, waves, CAUSAL, ATOMIC>;
     # dropout kernels are not classified
     if targs[-1] == "true" and kind in ("fwd", "dq", "dkdv"):
         return None
     if kind == "dkdv_wide":
-        causal, atomic = targs[3] == "true", targs[4] == "true"
+        causal, atomic = targs[4] == "true", targs[5] == "true"
         return ("dkdv_atomic" if atomic else "dkdv"), ("causal" if causal else "full")
     if kind == "fwd":
         return "fwd", ("causal" if targs[5] == "true" else "full")
