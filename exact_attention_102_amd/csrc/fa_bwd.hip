@@ -338,15 +338,20 @@ struct DkdvMath {
         // feed their own dK/dV columns, which are never stored -- except through dS in
         // the atomic dQ product, where their dS^T rows are written as zeros below.
         // Under the causal mask, key > query covers them as well.
-        const bool need_mask = CAUSAL && qbase < kw + 31;
+        // causal: scores of keys after the query are -inf (P = 0), in a pass of its own
+        // that only diagonal blocks take (the empty asm keeps it a branch)
+        if (CAUSAL && qbase < kw + 31) {
+          asm volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
+            if (key > q) s[r] = -INFINITY;
+          }
+        }
         f32x16 p, ds;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pv = exp2_hw(fmaf(s[r], c, -l2[r]));
-          if (need_mask) {
-            const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
-            if (key > q) pv = 0.f;
-          }
+          const float pv = exp2_hw(fmaf(s[r], c, -l2[r]));
           p[r] = pv;
           float dpv = dp[r];
           if constexpr (DROP) dpv = drop_keep(dr[r >> 3], r & 7, dc.t) ? dpv * ks : 0.f;
@@ -689,16 +694,18 @@ struct DkdvWideMath {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int kb = key + 32 * b;
-          const bool need_mask = CAUSAL && qbase < kw + 32 * b + 31;
+          // causal: scores of keys after the query are -inf (P = 0), in a pass of its own
+          // that only diagonal blocks take (the empty asm keeps it a branch)
+          if (CAUSAL && qbase < kw + 32 * b + 31) {
+            asm volatile("");
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float pv = exp2_hw(fmaf(p[b][r], c, -l2[r]));
-            if (need_mask) {
+            for (int r = 0; r < 16; ++r) {
               const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
-              if (kb > q) pv = 0.f;
+              if (kb > q) p[b][r] = -INFINITY;
             }
-            p[b][r] = pv;
           }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) p[b][r] = exp2_hw(fmaf(p[b][r], c, -l2[r]));
           pb[b][0] = pack8(p[b], 0);
           pb[b][1] = pack8(p[b], 8);
         }
@@ -1062,14 +1069,21 @@ struct DqMath {
         dp = mfma32(fvr.row(vt, kb * 32, kk), dof[kk], dp);
         fence_every<4>(kk);
       }
+      // keys past the end, and (causal) keys after the query, score -inf (P = 0).  A
+      // pass of its own, taken only on tiles that need it; the empty asm statement
+      // keeps it a branch (speculated, it becomes per-element selects on every tile).
+      if (need_mask) {
+        asm volatile("");
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kidx = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
+          if (kidx >= N || (CAUSAL && kidx > qi)) s[r] = -INFINITY;
+        }
+      }
       f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2_hw(fmaf(s[r], c, -lse2));
-        if (need_mask) {
-          const int kidx = k0 + kb * 32 + 16 * (r >> 3) + 8 * g + (r & 7);
-          if (kidx >= N || (CAUSAL && kidx > qi)) pv = 0.f;
-        }
+        const float pv = exp2_hw(fmaf(s[r], c, -lse2));
         float dpv = dp[r];
         if constexpr (DROP) dpv = drop_keep(dr[2 * kb + (r >> 3)], r & 7, dc.t) ? dpv * ks : 0.f;
         ds[r] = pv * (dpv - dl);
