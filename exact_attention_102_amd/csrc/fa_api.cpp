@@ -92,8 +92,8 @@ int default_index(int pass, int d, int causal) {
     case 2:  // dkdv + atomic dq, K read from LDS, dQ one tile late: d64 Bk32x8 Bq64, causal d96 Bk32x8 Bq32,
              // d192 and d256 Bk32x4 Bq32; d128 and non-causal d96 two key blocks per wave, Bk64x4 Bq32
       return d == 64 ? 4 : d == 128 ? 4 : d == 96 ? (causal ? 1 : 2) : 1;
-    case 3:                                           // dq: d128 non-causal Bq32x8 Bc64, d96 causal Bq32x8
-      return ((d == 128 && !causal) ? 2 : 0) + ((d == 96 && causal) ? 1 : 0);
+    case 3:  // dq: d128 Bq32x8 Bc64 (both masks), the others Bq32x4 (d256, d192: Bc32)
+      return d == 128 ? 2 : 0;
     default: return -1;
   }
 }
