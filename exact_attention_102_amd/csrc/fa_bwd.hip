@@ -10,6 +10,11 @@
 // sum_k dO_ik O_ik (the preprocess kernel); dV = P^T dO; dK = scale * dS^T Q;
 // dQ = scale * dS K.
 //
+// Kernels: preprocess_kernel (delta, dq zeroing); dkdv_kernel (one 32-key block per
+// wave; both designs, every head dim, dropout); dkdv_wide_kernel (two 32-key blocks
+// per wave, so each Q/dO fragment read from LDS feeds two MFMAs; both designs, head
+// dims 64, 96, 128, no dropout); dq_kernel (the 7-GEMM dQ pass).
+//
 // DROP: dropout on P (fa_dropout.h).  With M the keep mask and s the keep scale,
 // the forward used Pd = P * M * s, so dV = Pd^T dO and dP = (dO V^T) * M * s, while
 // dS = P * (dP - delta_i) keeps its form: delta_i = rowsum(Pd * dO V^T) =
