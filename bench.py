@@ -1,13 +1,15 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[,NAME...]] [--no-cpu-baseline]
 
-One step runs the whole path over the workload's synthetic bf16 inputs (already
-resident in HBM): for the non-causal and the causal mask, the forward, the
-5-GEMM backward (preprocess with dq zeroing, dK/dV kernel with fp32-atomic dQ)
-and the 7-GEMM backward (preprocess, dK/dV kernel, dQ kernel).  Every kernel is
-bracketed by HIP events on the stream it runs on; W untimed steps are followed
-by exactly K timed steps between two device synchronisations.
+One step runs the whole path over every workload's synthetic bf16 inputs (already
+resident in HBM) -- by default both head-dim-128 workloads of the metric, B4 H16
+N2048 (non-causal and causal) and B2 H16 N8192 (causal): for each workload and
+mask, the forward, the 5-GEMM backward (preprocess with dq zeroing, dK/dV kernel
+with fp32-atomic dQ) and the 7-GEMM backward (preprocess, dK/dV kernel, dQ
+kernel).  Every kernel is bracketed by HIP events on the stream it runs on; W
+untimed steps are followed by exactly K timed steps between two device
+synchronisations.
 
 Work accounting (masked tiles are not credited; pairs = unmasked score
 elements): forward 4 d pairs, backward 10 d pairs for either design (the
@@ -85,8 +87,9 @@ def atomic_adds_per_launch(B, H, N, d, causal, bk, bq):
     return B * H * rows * d
 
 
-def atomic_ceiling(w):
-    """fp32 atomics per second that the committed probe summary measured for this shape, or None."""
+def atomic_ceiling(d):
+    """fp32 atomics per second that the committed probe summary measured for the default atomic pattern at head
+    dim d (buffer atomics, no cache-policy bits, key tiles of a head on one XCD), or None."""
     path = os.path.join(ROOT, "profiles", "atomic_dq_probe.md")
     if not os.path.exists(path):
         return None
@@ -95,14 +98,14 @@ def atomic_ceiling(w):
             if not line.startswith("{"):
                 continue
             rec = json.loads(line)
-            if rec.get("probe") == "fp32 atomic add" and (rec["B"], rec["H"], rec["N"], rec["d"]) == (w.B, w.H, w.N,
-                                                                                                     w.d):
+            if rec.get("probe") == "buffer aux=0" and rec.get("mapping") == "xcd" and rec["d"] == d:
                 return rec["G_per_s"]
     return None
 
 
-def cpu_baseline(w, causal_modes, heads):
-    """The fp64 oracle as it stands, timed on this host's cores over `heads` heads of the workload."""
+def cpu_baseline(cases, heads_per_workload=-1):
+    """The fp64 oracle as it stands, timed on this host's cores over the step's cases (every head of each
+    workload, or the first `heads_per_workload`)."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -110,21 +113,78 @@ def cpu_baseline(w, causal_modes, heads):
     from exact_attention_102_amd.flops import attention_flops
 
     cores = oracle.usable_cores()
-    workers = max(1, min(cores, len(heads)))
-    blas = max(1, cores // workers)
-    q, k, v, do = (workloads.bf16_to_f64(workloads.to_bf16(x)) for x in workloads.draw_workload(w))
-    flops = 0
+    flops, parts, used = 0, [], 1
+    host = {}
+    for case in cases:
+        if case.w.name not in host:
+            host[case.w.name] = [workloads.bf16_to_f64(workloads.to_bf16(x)) for x in workloads.draw_workload(case.w)]
     t0 = time.perf_counter()
-    with threadpool_limits(limits=blas, user_api="blas"):
-        for causal in causal_modes:
-            oracle.attention_forward_batched(q, k, v, w.scale, causal, workers=workers, heads=heads)
-            oracle.attention_backward_batched(q, k, v, do, w.scale, causal, workers=workers, heads=heads)
-            f = attention_flops(1, len(heads), w.N, w.d, causal)
-            flops += f["fwd"] + f["bwd_effective"]
+    for case in cases:
+        w = case.w
+        nh = w.B * w.H if heads_per_workload < 0 else min(heads_per_workload, w.B * w.H)
+        heads = list(range(nh))
+        workers = max(1, min(cores, len(heads)))
+        blas = max(1, cores // workers)
+        used = max(used, workers * blas)
+        q, k, v, do = host[w.name]
+        with threadpool_limits(limits=blas, user_api="blas"):
+            oracle.attention_forward_batched(q, k, v, w.scale, case.causal, workers=workers, heads=heads)
+            oracle.attention_backward_batched(q, k, v, do, w.scale, case.causal, workers=workers, heads=heads)
+        f = attention_flops(1, len(heads), w.N, w.d, case.causal)
+        flops += f["fwd"] + f["bwd_effective"]
+        parts.append("%d of %d heads of %s" % (len(heads), w.B * w.H, case.key))
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers * blas, "kind": "oracle",
-            "sample": "%d of %d heads of %s, masks %s, fwd+bwd in fp64 numpy, %.1f s wall" % (
-                len(heads), w.B * w.H, w.name, "+".join("causal" if c else "full" for c in causal_modes), dt)}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": used, "kind": "oracle",
+            "sample": "%s; fwd+bwd in fp64 numpy, %.1f s wall" % ("; ".join(parts), dt)}
+
+
+DEFAULT_WORKLOADS = "b4_h16_n2048_d128,b2_h16_n8192_d128_causal"
+KERNELS = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]
+
+
+class Case:
+    """One (workload, mask) of the step: its device inputs and outputs."""
+
+    def __init__(self, w, causal, dev_inputs):
+        import torch
+        self.w, self.causal = w, causal
+        self.mask = "causal" if causal else "full"
+        self.key = "%s/%s" % (w.name, self.mask)
+        B, H, N, d = w.B, w.H, w.N, w.d
+        self.q, self.k, self.v, self.do = dev_inputs
+        f32 = dict(dtype=torch.float32, device=self.q.device)
+        self.o = torch.empty((B, H, N, d), **f32)
+        self.lse = torch.empty((B, H, N), **f32)
+        self.delta = torch.empty((B, H, N), **f32)
+        self.dq5, self.dk5, self.dv5 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+        self.dq7, self.dk7, self.dv7 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+
+    def run(self, stream, ev):
+        """fwd | preprocess5 | dkdv_atomic | preprocess7 | dkdv | dq, events ev[0..6] around them."""
+        from exact_attention_102_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_fwd
+        w, c = self.w, self.causal
+        if ev:
+            ev[0].record(stream)
+        fa_fwd(self.q, self.k, self.v, c, w.scale, o=self.o, lse=self.lse, stream=stream)
+        if ev:
+            ev[1].record(stream)
+        fa_bwd_preprocess(self.o, self.do, delta=self.delta, dq=self.dq5, stream=stream)
+        if ev:
+            ev[2].record(stream)
+        fa_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.delta, c, w.scale, True, self.dk5, self.dv5,
+                    dq=self.dq5, stream=stream)
+        if ev:
+            ev[3].record(stream)
+        fa_bwd_preprocess(self.o, self.do, delta=self.delta, stream=stream)
+        if ev:
+            ev[4].record(stream)
+        fa_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.delta, c, w.scale, False, self.dk7, self.dv7,
+                    stream=stream)
+        if ev:
+            ev[5].record(stream)
+        fa_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.delta, c, w.scale, self.dq7, stream=stream)
+        if ev:
+            ev[6].record(stream)
 
 
 def main():
@@ -132,9 +192,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="b4_h16_n2048_d128")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOADS,
+                    help="comma-separated workload names (workloads.WORKLOADS)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=-1, help="heads in the oracle sample (-1: all)")
+    ap.add_argument("--cpu-heads", type=int, default=-1, help="heads per workload in the oracle sample (-1: all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (heads shard with no "
@@ -144,59 +205,29 @@ def main():
     import torch
 
     import workloads
-    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_config_name,
-                                         fa_default_config, fa_fwd, lib)
+    from exact_attention_102_amd import fa_config_name, fa_default_config, lib
     from exact_attention_102_amd.flops import attention_flops, mfa_op_counts
 
     lib()  # fail loudly if libfa.so is missing
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
-    w = workloads.WORKLOADS[args.workload]
-    B, H, N, d = w.B, w.H, w.N, w.d
-    masks = [False, True] if not w.causal else [True]
-    log("workload %s B=%d H=%d N=%d d=%d masks=%s" % (w.name, B, H, N, d, masks))
-
-    q, k, v, do = (workloads.to_bf16(x).cuda() for x in workloads.draw_workload(w))
-    dev = torch.device("cuda")
-    f32 = dict(dtype=torch.float32, device=dev)
-    o = torch.empty((B, H, N, d), **f32)
-    lse = torch.empty((B, H, N), **f32)
-    delta = torch.empty((B, H, N), **f32)
-    dq5, dk5, dv5 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
-    dq7, dk7, dv7 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
+    wls = [workloads.WORKLOADS[n] for n in args.workload.split(",") if n]
+    cases = []
+    for w in wls:
+        log("workload %s B=%d H=%d N=%d d=%d" % (w.name, w.B, w.H, w.N, w.d))
+        dev = tuple(workloads.to_bf16(x).cuda() for x in workloads.draw_workload(w))
+        for causal in ([False, True] if not w.causal else [True]):
+            cases.append(Case(w, causal, dev))
     stream = torch.cuda.current_stream()
 
-    # event plan per mask: fwd | pre5 | dkdv_atomic | pre7 | dkdv | dq
-    kernels = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]
-
     def step(record):
-        for mi, causal in enumerate(masks):
-            ev = record[mi] if record is not None else None
-            if ev:
-                ev[0].record(stream)
-            fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse, stream=stream)
-            if ev:
-                ev[1].record(stream)
-            fa_bwd_preprocess(o, do, delta=delta, dq=dq5, stream=stream)
-            if ev:
-                ev[2].record(stream)
-            fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, True, dk5, dv5, dq=dq5, stream=stream)
-            if ev:
-                ev[3].record(stream)
-            fa_bwd_preprocess(o, do, delta=delta, stream=stream)
-            if ev:
-                ev[4].record(stream)
-            fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, False, dk7, dv7, stream=stream)
-            if ev:
-                ev[5].record(stream)
-            fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq7, stream=stream)
-            if ev:
-                ev[6].record(stream)
+        for ci, case in enumerate(cases):
+            case.run(stream, record[ci] if record is not None else None)
 
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in masks] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in cases] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -205,57 +236,59 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # per (mask, kernel) mean duration in ms
+    # per (case, kernel) mean duration in ms over the K timed steps
     dur = {}
-    for mi, causal in enumerate(masks):
-        mname = "causal" if causal else "full"
-        for ki, kn in enumerate(kernels):
-            ts = [events[s][mi][ki].elapsed_time(events[s][mi][ki + 1]) for s in range(args.steps)]
-            dur[(mname, kn)] = (sum(ts) / len(ts), min(ts))
+    for ci, case in enumerate(cases):
+        for ki, kn in enumerate(KERNELS):
+            ts = [events[s][ci][ki].elapsed_time(events[s][ci][ki + 1]) for s in range(args.steps)]
+            dur[(case.key, kn)] = sum(ts) / len(ts)
 
     total_flops = 0
     passes = {}
     best = None
-    for causal in masks:
-        mname = "causal" if causal else "full"
-        fl = attention_flops(B, H, N, d, causal)
+    for case in cases:
+        w = case.w
+        fl = attention_flops(w.B, w.H, w.N, w.d, case.causal)
         p = fl["pairs"]
-        t_fwd = dur[(mname, "fwd")][0]
-        t_b5 = dur[(mname, "preprocess5")][0] + dur[(mname, "dkdv_atomic")][0]
-        t_b7 = dur[(mname, "preprocess7")][0] + dur[(mname, "dkdv")][0] + dur[(mname, "dq")][0]
+        t_fwd = dur[(case.key, "fwd")]
+        t_b5 = dur[(case.key, "preprocess5")] + dur[(case.key, "dkdv_atomic")]
+        t_b7 = dur[(case.key, "preprocess7")] + dur[(case.key, "dkdv")] + dur[(case.key, "dq")]
         total_flops += fl["fwd"] + 2 * fl["bwd_effective"]
-        passes[mname] = {
+        ent = {
             "fwd_tflops": fl["fwd"] / t_fwd / 1e9, "fwd_ms": t_fwd,
             "bwd_5gemm_tflops": fl["bwd_effective"] / t_b5 / 1e9, "bwd_5gemm_ms": t_b5,
             "bwd_7gemm_tflops": fl["bwd_effective"] / t_b7 / 1e9, "bwd_7gemm_ms": t_b7,
             "bwd_7gemm_issued_tflops": fl["bwd_7gemm_issued"] / t_b7 / 1e9,
-            "kernel_ms": {kn: round(dur[(mname, kn)][0], 4) for kn in kernels},
+            "kernel_ms": {kn: round(dur[(case.key, kn)], 4) for kn in KERNELS},
             "pairs": p,
+            "mfa_op_counts_per_dispatch": mfa_op_counts(w.N, w.d),
         }
         for key in ("fwd", "bwd_5gemm", "bwd_7gemm"):
-            passes[mname][key + "_pct_peak"] = 100.0 * passes[mname][key + "_tflops"] / PEAK_BF16_TFLOPS
-        passes[mname]["faster_bwd"] = "5gemm" if t_b5 <= t_b7 else "7gemm"
-        passes[mname]["t7_over_t5"] = t_b7 / t_b5
+            ent[key + "_pct_peak"] = 100.0 * ent[key + "_tflops"] / PEAK_BF16_TFLOPS
+        ent["faster_bwd"] = "5gemm" if t_b5 <= t_b7 else "7gemm"
+        ent["t7_over_t5"] = t_b7 / t_b5
+        passes[case.key] = ent
+        # the dominant kernel: the one that takes the most time per step
         for kn in ("fwd", "dkdv_atomic", "dkdv", "dq"):
-            t = dur[(mname, kn)][0]
+            t = dur[(case.key, kn)]
             if best is None or t > best[2]:
-                best = (kn, mname, t, kernel_flops(kn, d, p))
-    op_counts = mfa_op_counts(N, d)
+                best = (kn, case, t, kernel_flops(kn, w.d, p))
 
-    kn, mname, t_ms, kflops = best
+    kn, case, t_ms, kflops = best
+    w = case.w
     achieved = kflops / (t_ms * 1e-3) / 1e12
-    traffic = stored_traffic(kn, mname, w.name)
+    traffic = stored_traffic(kn, case.mask, w.name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "%s (%s mask)" % (kn, mname), "launch_ms": round(t_ms, 4),
+                "kernel": "%s (%s, %s mask)" % (kn, w.name, case.mask), "launch_ms": round(t_ms, 4),
                 "flops_per_launch": kflops}
     if kn == "dkdv_atomic":
-        # the fused dQ atomics, not the MFMAs, bound this kernel: its rate against the probe's ceiling
+        # the fused dQ atomics, not only the MFMAs, bound this kernel: their rate against the probe's ceiling
         from exact_attention_102_amd.report import tile_shape
-        bk, bq = tile_shape(fa_config_name(2, d, mname == "causal", fa_default_config(2, d, mname == "causal")))
-        adds = atomic_adds_per_launch(B, H, N, d, mname == "causal", bk, bq)
+        bk, bq = tile_shape(fa_config_name(2, w.d, case.causal, fa_default_config(2, w.d, case.causal)))
+        adds = atomic_adds_per_launch(w.B, w.H, w.N, w.d, case.causal, bk, bq)
         rate = adds / (t_ms * 1e-3) / 1e9
-        ceil = atomic_ceiling(w)
+        ceil = atomic_ceiling(w.d)
         roofline["atomics"] = {"adds_per_launch": adds, "achieved_G_per_s": round(rate, 1),
                                "probe_ceiling_G_per_s": ceil,
                                "frac": round(rate / ceil, 4) if ceil else None}
@@ -263,24 +296,28 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        heads = list(range(B * H)) if args.cpu_heads < 0 else list(range(min(args.cpu_heads, B * H)))
-        log("timing the fp64 oracle on %d heads" % len(heads))
-        cpu = cpu_baseline(w, masks, heads)
+        log("timing the fp64 oracle")
+        cpu = cpu_baseline(cases, args.cpu_heads)
 
-    cfgs = {"fwd": fa_config_name(0, d, False, fa_default_config(0, d)),
-            "dkdv": fa_config_name(1, d, False, fa_default_config(1, d)),
-            "dkdv_atomic": fa_config_name(2, d, False, fa_default_config(2, d)),
-            "dq": fa_config_name(3, d, False, fa_default_config(3, d))}
+    tiles = {}
+    for wd in sorted({w.d for w in wls}):
+        for causal in (False, True):
+            m = "causal" if causal else "full"
+            tiles["d%d_%s" % (wd, m)] = {
+                "fwd": fa_config_name(0, wd, causal, fa_default_config(0, wd, causal)),
+                "dkdv": fa_config_name(1, wd, causal, fa_default_config(1, wd, causal)),
+                "dkdv_atomic": fa_config_name(2, wd, causal, fa_default_config(2, wd, causal)),
+                "dq": fa_config_name(3, wd, causal, fa_default_config(3, wd, causal))}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name + (" (non-causal + causal)" if len(masks) == 2 else ""), "B": B, "H": H,
-                   "N": N, "d": d, "scale": w.scale, "step": "per mask: fwd + 5-GEMM bwd + 7-GEMM bwd",
-                   "tiles": cfgs},
+        "config": {"workload": " + ".join(c.key for c in cases),
+                   "workloads": [{"name": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "scale": w.scale}
+                                 for w in wls],
+                   "step": "per workload and mask: fwd + 5-GEMM bwd + 7-GEMM bwd", "tiles": tiles},
         "passes": {m: {k2: (round(v2, 4) if isinstance(v2, float) else v2) for k2, v2 in p.items()}
                    for m, p in passes.items()},
-        "mfa_op_counts_per_dispatch": op_counts,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -34,13 +34,17 @@ Range rng(const void* p, size_t bytes) { return Range{static_cast<const char*>(p
 bool supported_d(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
 
 // Shared size checks: positive sizes, 32-bit grid and row counts, 64-bit byte counts.
+// One head of a bf16 input (N * d * 2 bytes) must stay below 2^31 bytes: the tile
+// copies address a head through a buffer range of that size and zero-fill the
+// padded columns of d = 96 / 192 through an offset of 2^31, which has to lie
+// outside every range.
 fa_status check_sizes(int B, int H, int N, int d, float scale) {
   if (B <= 0 || H <= 0 || N <= 0) return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
   if (!supported_d(d)) return FA_ERR_UNSUPPORTED;
   const long long rows = (long long)B * H * N;
   if (rows > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  if ((long long)N * d > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)N * d * 2 >= 0x80000000LL) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 

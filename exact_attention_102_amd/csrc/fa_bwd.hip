@@ -819,10 +819,11 @@ struct DkdvWideMath {
   // dQ_tile = dS K over the workgroup's BK keys (its dS^T blocks in LDS, written by
   // tile() of the previous query tile and made visible by the barrier that ended it),
   // one fp32 atomic per dq element; the waves split the (query block, d block) pairs.
-  // The adds are buffer atomics over the head's N x D accumulator: one 32-bit lane
-  // offset per pair, the per-register row steps in the scalar and immediate offsets,
-  // and rows past the end beyond the buffer range (N * DV * 4 + 32 rows fit 32 bits;
-  // the launcher checks).
+  // The adds are buffer atomics over the head's N x DV accumulator.  The whole row
+  // offset of every add sits in the vector offset (plus an immediate of at most
+  // 3 DV * 4 bytes): the buffer range check covers the vector and immediate offsets
+  // but not the scalar one, and it is what drops the adds of rows past the end
+  // ((N + 32) * DV * 4 fits 32 bits; the launcher checks).
   __device__ __forceinline__ static void atomic_dq(const LDS char* dst, const LDS char* ktile, float* dqh, int q0,
                                                    int N, float scale, int wave, int g, int l32, int lane) {
     const __amdgpu_buffer_rsrc_t rs =
@@ -840,10 +841,11 @@ struct DkdvWideMath {
       }
       // register r holds row q0 + 32 qb + 4 g + 8 (r / 4) + r % 4, column 32 db + l32
       const unsigned off = ((unsigned)(q0 + qb * 32 + 4 * g) * DV + db * 32 + l32) * 4u;
+      static_assert(3 * DV * 4 < 4096, "the row step r % 4 must fit the 12-bit immediate offset");
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rs, off + (r & 3) * (DV * 4),
-                                                        8 * (r >> 2) * (DV * 4), 0);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * scale, rs,
+                                                        off + (unsigned)(8 * (r >> 2) + (r & 3)) * (DV * 4), 0, 0);
     }
   }
 

@@ -121,6 +121,19 @@ def test_bwd_rejects_bad_arguments(L):
                                None, 1, None) == FA_ERR_INVALID_ARG   # zero_dq without dq
 
 
+def test_heads_of_2gib_or_more_rejected(L):
+    """One head of a bf16 input must stay below 2^31 bytes (N * d * 2): the tile copies
+    address a head through one 32-bit buffer range and zero-fill the padded columns of
+    d = 96 / 192 through an offset of 2^31, which must fall outside that range."""
+    from exact_attention_102_amd import FA_ERR_INVALID_ARG
+    for d in (64, 96, 128, 192, 256):
+        n_limit = -(-(1 << 31) // (2 * d))       # smallest N with N * d * 2 >= 2^31
+        assert fwd(L, N=n_limit, d=d) == FA_ERR_INVALID_ARG
+        assert bwd(L, N=n_limit, d=d, ws_bytes=1 << 40) == FA_ERR_INVALID_ARG
+        assert L.fa_bwd_workspace_size(1, 1, n_limit, d, 1) == 0
+        assert L.fa_bwd_workspace_size(1, 1, n_limit - 1, d, 1) > 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     from exact_attention_102_amd import binding
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
