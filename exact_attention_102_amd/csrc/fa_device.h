@@ -157,11 +157,16 @@ struct ColOffsets {
 
 // One direct-to-LDS copy instruction (buffer_load_dwordx4 ... lds): lane l reads 16
 // bytes at rsrc.base + soff + voff and writes them to LDS at lds + 16 l (M0 holds
-// the LDS base; s_nop covers the M0-write -> LDS-DMA hazard).  M0 is written inside
-// the statement and declared clobbered; nothing else in these kernels uses M0 (no
-// LDS-DMA builtins, GWS or indexed register moves).  Passing the base as an "{m0}"
-// operand instead leaves the compiler short of SGPRs (every tile's LDS base stays
-// live in one), and that build faulted the GPU, so it is not used.
+// the LDS base; the s_nop is the wait state the hardware needs between a scalar
+// write of M0 and an LDS-DMA instruction reading it).  M0 is written inside the
+// statement and declared clobbered; nothing else in these kernels uses M0 (no
+// LDS-DMA builtins, GWS or indexed register moves; the compiled code holds M0 only
+// in these statements), so the compiler's warning about clobbering a reserved
+// register has nothing to break.  The base must not be passed as an "{m0}" operand:
+// the compiler then writes M0 itself right before the statement, and its hazard
+// recognizer cannot see the LDS-DMA load inside, so no wait state separates the two
+// and the load may use the previous M0 -- an LDS address outside the tile, possibly
+// outside the workgroup's allocation.  A build of that form faulted the GPU.
 //
 // It is issued from inline assembly on purpose.  Through the compiler builtins,
 // either form (global_load_lds, buffer_load ... lds) damages the wait-count

@@ -1,10 +1,17 @@
 """Markdown summaries of rocprofv3 output for the profiles/ folder.
 
     python -m exact_attention_102_amd.profsum stats <prof_dir> --command "<cmd>" --title "<t>" --out F
+    python -m exact_attention_102_amd.profsum trace <prof_dir> --bench <bench.json> --steps K --warmup W \
+        --command "<cmd>" --out F
     python -m exact_attention_102_amd.profsum sq <pmc_dir> --workload b4_h16_n2048_d128 --command "<cmd>" --out F
 
 `stats` turns the `*_kernel_stats.csv` of a `rocprofv3 --kernel-trace --stats` run into a
-table of calls and durations per kernel.  `sq` turns the `*_counter_collection.csv` of a
+table of calls and durations per kernel.  `trace` reads the same run's `*_kernel_trace.csv`
+together with the JSON line bench.py printed in that run: it assigns every dispatch to
+its (workload, mask, kernel) by its position in the step, averages the K timed steps
+(the W warm-up steps excluded, as bench.py's event means are) and sets the result beside
+bench.py's event-timed mean, then recomputes the roofline of bench.py's dominant kernel
+from the trace.  `sq` turns the `*_counter_collection.csv` of a
 `rocprofv3 --pmc SQ_... GRBM_GUI_ACTIVE` run over `traffic.py --run` (one launch of each
 kernel per mask) into per-kernel MFMA busy fraction, MFMA flops, VALU and transcendental
 instructions per score element and the LDS bank-conflict ratio.
@@ -14,6 +21,7 @@ from __future__ import annotations
 import argparse
 import csv
 import glob
+import json
 import os
 import sys
 
@@ -55,6 +63,53 @@ def stats_table(prof_dir: str) -> str:
     return "\n".join(out)
 
 
+KERNEL_ORDER = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]   # bench.py's step order
+
+
+def trace_table(prof_dir: str, bench_json: str, steps: int, warmup: int) -> str:
+    with open(bench_json) as fh:
+        bench = json.loads([l for l in fh if l.startswith("{")][-1])
+    cases = list(bench["passes"])
+    per_step = len(KERNEL_ORDER) * len(cases)
+    rows = []
+    with open(_one(prof_dir, "kernel_trace.csv")) as fh:
+        for r in csv.DictReader(fh):
+            name = _col(r, "Kernel_Name", "KernelName")
+            if "fa::" not in name:
+                continue
+            rows.append((int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp")), name))
+    rows.sort()
+    if len(rows) != (steps + warmup) * per_step:
+        raise ValueError("%d attention dispatches in the trace, expected (%d + %d) x %d"
+                         % (len(rows), warmup, steps, per_step))
+    timed = rows[warmup * per_step:]
+    acc = {}
+    for i, (t0, t1, name) in enumerate(timed):
+        pos = i % per_step
+        key = (cases[pos // len(KERNEL_ORDER)], KERNEL_ORDER[pos % len(KERNEL_ORDER)])
+        acc.setdefault(key, [name, []])[1].append((t1 - t0) / 1e3)
+    out = ["| workload / mask | kernel | trace mean us (K timed steps) | trace min us | bench.py event mean us | "
+           "trace / event |", "|---|---|---|---|---|---|"]
+    for (case, kn), (name, ds) in acc.items():
+        mean = sum(ds) / len(ds)
+        ev = bench["passes"][case]["kernel_ms"][kn] * 1e3
+        out.append("| %s | `%s` (%s) | %.1f | %.1f | %.1f | %.3f |" % (case, name, kn, mean, min(ds), ev, mean / ev))
+    rf = bench["roofline"]
+    dom = rf["kernel"]  # "kernel (workload, mask mask)"
+    kn = dom.split(" (")[0]
+    wl, mask = dom.split(" (")[1].rstrip(")").split(", ")
+    case = "%s/%s" % (wl, mask.split()[0])
+    ds = acc[(case, kn)][1]
+    mean_us = sum(ds) / len(ds)
+    achieved = rf["flops_per_launch"] / (mean_us * 1e-6) / 1e12
+    out += ["", "Roofline of bench.py's dominant kernel, %s: %.4g flop per launch / %.1f us (trace mean) = "
+            "%.1f TFLOP/s = %.4f of %.0f; bench.py reported %.1f TFLOP/s = %.4f from its event mean of %.1f us "
+            "(trace / event %.3f)." % (dom, rf["flops_per_launch"], mean_us, achieved, achieved / rf["peak"],
+                                       rf["peak"], rf["achieved"], rf["frac"], rf["launch_ms"] * 1e3,
+                                       mean_us / (rf["launch_ms"] * 1e3))]
+    return "\n".join(out)
+
+
 def sq_table(pmc_dir: str, workload: str) -> str:
     from exact_attention_102_amd.traffic import classify
     from workloads import WORKLOADS
@@ -93,17 +148,23 @@ def sq_table(pmc_dir: str, workload: str) -> str:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["stats", "sq"])
+    ap.add_argument("kind", choices=["stats", "trace", "sq"])
     ap.add_argument("dir")
     ap.add_argument("--workload", default="b4_h16_n2048_d128")
     ap.add_argument("--command", required=True, help="the profiler command that produced dir")
     ap.add_argument("--title", default=None)
     ap.add_argument("--note", default="")
     ap.add_argument("--out", required=True)
+    ap.add_argument("--bench", default=None, help="trace: the JSON line bench.py printed in the profiled run")
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     a = ap.parse_args()
     if a.kind == "stats":
         title = a.title or "rocprofv3 kernel stats: " + a.workload
         body = stats_table(a.dir)
+    elif a.kind == "trace":
+        title = a.title or "rocprofv3 kernel trace of bench.py, per workload, mask and kernel"
+        body = trace_table(a.dir, a.bench, a.steps, a.warmup)
     else:
         title = a.title or "rocprofv3 SQ counters: %s (one launch of each kernel per mask)" % a.workload
         body = sq_table(a.dir, a.workload)
