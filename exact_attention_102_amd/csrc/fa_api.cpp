@@ -85,9 +85,11 @@ int count_for_d(const Cfg* t, int n, int d) {
 int default_index(int pass, int d, int causal) {
   switch (pass) {
     case 0:  // fwd: d64 Br32x4 Bc64 at three waves per SIMD (causal: Br32x8 Bc64), d96 Br32x8 Bc64, d128
-             // Br32x4 Bc32 at three waves per SIMD, d192 Bc64, d256 Bc32; causal d96 Br32x4 Bc32 at three
-             // waves per SIMD, causal d192 Bc32
-      if (d == 128) return 4;
+             // optimistic statistics, Br32x4 Bc64 at two waves per SIMD (causal: Bc32 at three), d192 Bc64,
+             // d256 Bc32 with optimistic statistics; causal d96 Br32x4 Bc32 at three waves per SIMD, causal
+             // d192 Bc32
+      if (d == 128) return causal ? 5 : 6;
+      if (d == 256) return 2;
       if (causal && d == 96) return 2;
       return d == 64 ? (causal ? 2 : 4) : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
     case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d192 and d256 Bk32x4 Bq32, K read from LDS; d96

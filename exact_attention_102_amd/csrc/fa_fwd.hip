@@ -36,11 +36,14 @@
 namespace fa {
 
 constexpr float kRescaleSlack = 8.0f;
+// OPT: largest per-lane partial sum of P (over the lane's keys of one tile) accepted
+// against a stale running maximum; P itself then stays at most 2^12.
+constexpr float kOptLimit = 4096.0f;
 
 // D: width of the LDS tiles (64, 128, 256); DV <= D, a multiple of 32: the head-dim
 // columns actually computed (96 and 192 run on 128- and 256-wide tiles and skip the
 // products of the zero columns).
-template <int D, int DV, int BC, bool CAUSAL, bool DROP>
+template <int D, int DV, int BC, bool CAUSAL, bool DROP, bool OPT = false>
 struct FwdTileMath {
   static constexpr int KB = BC / 32;  // 32-key blocks per tile
   static constexpr int DB = DV / 32;  // 32-wide blocks of the computed head dim
@@ -52,7 +55,8 @@ struct FwdTileMath {
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
                                               f32x16 (&o)[DB], float& m_run, float& l_run, float& lb_run, int k0,
                                               int q_w, int qi, int N, float c, const RowOffsets<D, kRowOnly>& fk,
-                                              const ColOffsets<D, kColOnly>& fv, int g, const DropCtx& dc) {
+                                              const ColOffsets<D, kColOnly>& fv, int g, const DropCtx& dc,
+                                              bool first) {
     // draws of keys k0 + 32 kb + 16 h + 8 g + (0..7) for this lane's query
     u32x4 dr[DROP ? 2 * KB : 1];
     if constexpr (DROP) {
@@ -87,40 +91,71 @@ struct FwdTileMath {
         }
       }
     }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    }
-    mx = half_swap_max(mx) * c;
-    // Tile 0 holds key 0 <= every query, so m_run is finite after the first tile.
-    const bool grow = mx > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
-      const float alpha = exp2_hw(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      lb_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      }
-    }
-    const float nm = -m_run;
     bf16x8 pb[2 * KB];
     float rs = 0.f, rb = 0.f;
+    // OPT (optimistic statistics): after the first tile, P is computed against the running m
+    // without first taking the tile's row maximum; only if some lane's partial sum of P
+    // leaves (0, kOptLimit] (an element above the limit, an overflow, or a NaN) does the wave
+    // take the maximum and rescale, then recompute P.  The scores stay in s until that test.
+    if (OPT && !first) {
+      const float nm = -m_run;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float p8[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p8[e] = exp2_hw(fmaf(s[kb][8 * h + e], c, nm));
+            rs += p8[e];
+          }
+          bf16x8 b;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) b[e] = (__bf16)p8[e];
+          pb[2 * kb + h] = b;
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kOptLimit)) == 0) goto have_p;
+    }
+    {
+      float mx = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      mx = half_swap_max(mx) * c;
+      // Tile 0 holds key 0 <= every query, so m_run is finite after the first tile.
+      const bool grow = OPT ? mx > m_run : mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = exp2_hw(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        lb_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        }
+      }
+      const float nm = -m_run;
+      rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_hw(fmaf(s[kb][r], c, nm));
+          s[kb][r] = p;
+          rs += p;
+        }
+        pb[2 * kb] = pack8(s[kb], 0);
+        pb[2 * kb + 1] = pack8(s[kb], 8);
+      }
+    }
+  have_p:
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(fmaf(s[kb][r], c, nm));
-        s[kb][r] = p;
-        rs += p;
-      }
-      pb[2 * kb] = pack8(s[kb], 0);
-      pb[2 * kb + 1] = pack8(s[kb], 8);
       rb = sum_bf16x8(pb[2 * kb], rb);
       rb = sum_bf16x8(pb[2 * kb + 1], rb);
       if constexpr (DROP) {
@@ -148,9 +183,9 @@ struct FwdTileMath {
 
 // OCC: waves per SIMD the register allocation must allow (2 lets a second wave's
 // MFMAs overlap this wave's softmax; d = 256 needs the whole register file).
-template <int D, int DV, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
+template <int D, int DV, int BC, int NW, int OCC, bool CAUSAL, bool DROP, bool OPT>
 __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
-  using M = FwdTileMath<D, DV, BC, CAUSAL, DROP>;
+  using M = FwdTileMath<D, DV, BC, CAUSAL, DROP, OPT>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;  // bytes of one K or V tile
   constexpr int DB = M::DB, KK = M::KK;
@@ -222,7 +257,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       vdma.issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
     if (!CAUSAL || j * BC <= q_w + 31)
-      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g, dc);
+      M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g, dc, j == 0);
     wait_tile();
     __syncthreads();
     if (j + 1 >= nkt) break;
@@ -235,7 +270,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
     if (!CAUSAL || (j + 1) * BC <= q_w + 31)
-      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g, dc);
+      M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g, dc, false);
     wait_tile();
     __syncthreads();
   }
@@ -258,7 +293,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, int DV, int BC, int NW, int OCC, bool DROP = false>
+template <int D, int DV, int BC, int NW, int OCC, bool DROP = false, bool OPT = false>
 static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BR = 32 * NW;
   const int nqt = (a.N + BR - 1) / BR;
@@ -266,10 +301,10 @@ static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   if (blocks <= 0 || blocks > 0x7fffffff) return -1;
   if ((a.drop_t != 0) != DROP) return -1;
   if (causal) {
-    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, true, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, true, DROP, OPT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, false, DROP>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((fwd_kernel<D, DV, BC, NW, OCC, false, DROP, OPT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream,
                        a);
   }
   return 0;
@@ -282,6 +317,14 @@ static int launch_fwd(const FwdArgs& a, bool causal, hipStream_t stream) {
   {                                                                                                       \
     DV, 32 * (NW), BC, NW, "fwd d" #DV " (tiles " #D ") Br32x" #NW " Bc" #BC " occ" #OCC,               \
         &launch_fwd<D, DV, BC, NW, OCC>                                                                   \
+  }
+// optimistic statistics (OPT): the tile's row maximum is taken only when P leaves its bound
+#define FWD_CFGO(D, BC, NW, OCC) \
+  { D, 32 * (NW), BC, NW, "fwd d" #D " Br32x" #NW " Bc" #BC " occ" #OCC " opt", &launch_fwd<D, D, BC, NW, OCC, false, true> }
+#define FWD_CFGVO(D, DV, BC, NW, OCC)                                                                   \
+  {                                                                                                       \
+    DV, 32 * (NW), BC, NW, "fwd d" #DV " (tiles " #D ") Br32x" #NW " Bc" #BC " occ" #OCC " opt",        \
+        &launch_fwd<D, DV, BC, NW, OCC, false, true>                                                      \
   }
 #define FWD_DROP_CFG(D, DV, BC, NW, OCC)                                                                \
   {                                                                                                       \
@@ -298,6 +341,9 @@ const FwdConfig* fwd_configs(int* count) {
       FWD_CFGV(128, 96, 64, 4, 2), FWD_CFGV(128, 96, 64, 8, 2), FWD_CFGV(256, 192, 32, 4, 1),
       FWD_CFGV(256, 192, 64, 4, 1),
       FWD_CFG(128, 32, 4, 3),  FWD_CFG(64, 64, 4, 3),  FWD_CFG(64, 32, 4, 4), FWD_CFGV(128, 96, 32, 4, 3),
+      FWD_CFGO(128, 32, 4, 3), FWD_CFGO(64, 64, 4, 3), FWD_CFGO(64, 64, 8, 2), FWD_CFGO(256, 32, 4, 1),
+      FWD_CFGVO(128, 96, 32, 4, 3), FWD_CFGVO(128, 96, 64, 8, 2), FWD_CFGVO(256, 192, 64, 4, 1),
+      FWD_CFGVO(256, 192, 32, 4, 1), FWD_CFGO(128, 64, 4, 2),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
