@@ -9,5 +9,5 @@ from .binding import (FA_BWD_5GEMM_ATOMIC, FA_BWD_7GEMM, FA_ERR_HIP, FA_ERR_INVA
                       fa_default_config, fa_fwd, fa_num_configs, fa_status_string, fa_version, lib,
                       fa_fwd_general, fa_bwd_general, fa_fwd_general_workspace_size,
                       fa_bwd_general_workspace_size, FaStrides, FaDropout, fa_fwd_dropout, fa_bwd_dropout,
-                      fa_dropout_keep_scale)
+                      fa_dropout_keep_scale, fa_bwd_noalloc, FA_ERR_TOO_LARGE, FA_NOALLOC_MAX_ROWS)
 from .flops import attention_flops, mfa_op_counts, pairs  # noqa: F401

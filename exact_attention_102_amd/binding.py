@@ -17,6 +17,8 @@ FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_WORKSPACE = 3
 FA_ERR_HIP = 4
+FA_ERR_TOO_LARGE = 5
+FA_NOALLOC_MAX_ROWS = 1 << 23
 FA_BWD_5GEMM_ATOMIC = 0
 FA_BWD_7GEMM = 1
 PASS_FWD, PASS_DKDV, PASS_DKDV_ATOMIC, PASS_DQ = 0, 1, 2, 3
@@ -60,6 +62,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd.restype = i
     L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, sz, vp, i, i]
     L.fa_bwd_ex.restype = i
+    L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp]
+    L.fa_bwd_noalloc.restype = i
     L.fa_bwd_preprocess.argtypes = [vp, vp, i, i, i, i, vp, vp, i, vp]
     L.fa_bwd_preprocess.restype = i
     L.fa_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp, vp, vp, i]
@@ -234,6 +238,24 @@ def fa_bwd(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
     return res
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int, dq, dk, dv, stream=None):
+    """fa_bwd_noalloc: the backward with the library's fixed scratch instead of a workspace; the caller
+    provides every output (nothing is allocated here either).  Returns (dq, dk, dv)."""
+    torch = _torch()
+    if dq is None or dk is None or dv is None:
+        raise ValueError("fa_bwd_noalloc writes into caller-provided dq, dk, dv")
+    B, H, N, d = q.shape
+    ptr = [_check(q, "q", torch.bfloat16), _check(k, "k", torch.bfloat16, q.shape),
+           _check(v, "v", torch.bfloat16, q.shape), _check(o, "o", torch.float32, q.shape),
+           _check(lse, "lse", torch.float32, (B, H, N)), _check(dout, "dout", torch.bfloat16, q.shape)]
+    pouts = [_check(t, n, torch.float32, q.shape) for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv"))]
+    st = lib().fa_bwd_noalloc(*ptr, B, H, N, d, int(bool(causal)), float(scale), int(variant), *pouts,
+                              _stream_ptr(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_noalloc")
+    return dq, dk, dv
 
 
 def fa_bwd_dropout(q, k, v, o, lse, dout, causal: bool, scale: float, p: float, seed: int, offset: int = 0,

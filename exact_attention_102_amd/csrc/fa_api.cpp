@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_launch.h"
@@ -176,6 +177,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head dimension, variant or configuration";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP launch error";
+    case FA_ERR_TOO_LARGE: return "FA_ERR_TOO_LARGE: B*H*N exceeds the fixed scratch of fa_bwd_noalloc";
   }
   return "FA_ERR_UNKNOWN";
 }
@@ -852,6 +854,60 @@ fa_status fa_bwd_general_dropout(const void* q, fa_strides q_str, const void* k,
   if (st != FA_OK) return st;
   return bwd_general_impl(q, q_str, k, k_str, v, v_str, o, o_str, lse, dout, dout_str, B, H, N, d, causal, scale,
                           variant, dq, dq_str, dk, dk_str, dv, dv_str, workspace, workspace_bytes, stream, &ds);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// fa_bwd_noalloc: fa_bwd whose delta scratch is a fixed device array instead of a
+// caller-provided workspace (for callers that cannot allocate).  The array's name is a
+// host-side stand-in in this file; kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) float scratch[FA_NOALLOC_MAX_ROWS];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch`, or nullptr (with the status) when it cannot be found.
+float* scratch_for_current_device(fa_status* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *st = FA_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      std::fprintf(stderr, "fa: hipGetSymbolAddress(scratch) failed on device %d: %s\n", dev, hipGetErrorString(e));
+      *st = FA_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dout, int B, int H, int N, int d, int causal, float scale,
+                         fa_bwd_variant variant, float* dq, float* dk, float* dv, void* stream) {
+  const fa_status sz = check_sizes(B, H, N, d, scale);
+  if (sz != FA_OK) return sz;
+  if ((long long)B * H * N > (long long)FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return FA_ERR_UNSUPPORTED;
+  fa_status st = FA_OK;
+  float* ws = scratch_for_current_device(&st);
+  if (!ws) return st;
+  return bwd_impl(q, k, v, o, lse, dout, B, H, N, d, causal, scale, variant, dq, dk, dv, ws,
+                  sizeof(float) * (size_t)FA_NOALLOC_MAX_ROWS, stream, -1, -1, nullptr);
 }
 
 }  // extern "C"

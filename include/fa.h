@@ -35,7 +35,9 @@
  *             scale, aliasing, or a tensor too large for 32-bit in-head indexing;
  *             FA_ERR_UNSUPPORTED: head dim not in {64, 96, 128, 192, 256} or unknown
  *             variant/config; FA_ERR_WORKSPACE: workspace missing or too small;
- *             FA_ERR_HIP: a launch failed (hipGetLastError after the launch).
+ *             FA_ERR_HIP: a launch failed (hipGetLastError after the launch);
+ *             FA_ERR_TOO_LARGE: the problem exceeds the fixed scratch of
+ *             fa_bwd_noalloc.
  *  Threads    stateless apart from a once-initialised device-property cache;
  *             safe to call from several host threads.
  */
@@ -53,7 +55,8 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
   FA_ERR_WORKSPACE = 3,
-  FA_ERR_HIP = 4
+  FA_ERR_HIP = 4,
+  FA_ERR_TOO_LARGE = 5
 } fa_status;
 
 typedef enum {
@@ -90,6 +93,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
                  const void* dout, int B, int H, int N, int d, int causal, float scale,
                  fa_bwd_variant variant, float* dq, float* dk, float* dv, void* workspace,
                  size_t workspace_bytes, void* stream);
+
+/* fa_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, semantics and kernels as fa_bwd; the backward's one scratch buffer,
+ * the fp32 row term delta [B,H,N], is a fixed array inside the library of
+ * FA_NOALLOC_MAX_ROWS floats (32 MiB) on each GPU it runs on, held until the process
+ * ends.  The array's address is looked up once per device, on the first call with that
+ * device current.  B*H*N above FA_NOALLOC_MAX_ROWS returns FA_ERR_TOO_LARGE before
+ * anything is enqueued.  The library allocates, frees and synchronises nothing.  All
+ * calls on one GPU share its array: calls whose work overlaps on one GPU (concurrent
+ * streams, host threads) race and must be serialised by the caller; each call writes
+ * every row of delta it later reads, so nothing needs clearing between calls. */
+#define FA_NOALLOC_MAX_ROWS (1u << 23)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const float* o, const float* lse,
+                         const void* dout, int B, int H, int N, int d, int causal, float scale,
+                         fa_bwd_variant variant, float* dq, float* dk, float* dv, void* stream);
 
 /* The backward's first step on its own: delta_i = sum_k dout_ik * o_ik per row
  * (the softmax-backward row term, computed from O instead of from P and dP; the
