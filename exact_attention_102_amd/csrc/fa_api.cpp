@@ -80,19 +80,21 @@ int count_for_d(const Cfg* t, int n, int d) {
 }
 
 // Default configuration per (pass, d, causal), chosen by the block-shape sweep
-// (exact_attention_102_amd/sweep.py) on the b4_h16_n2048_d128, b4_h8_n4096_d256 and
-// b1_h32_n16384_d64 workloads; an index among the pass's configurations for that d.
-// Head dims 96 and 192 were chosen on B4 H16 N2048 (both masks).
+// (exact_attention_102_amd/sweep.py --all: every head dim and mask on B4 H16 N2048 plus
+// the benchmark workloads at their own shapes); an index among the pass's
+// configurations for that d.  Where the shapes disagree, the benchmark workload of that
+// head dim decides (d64 causal: the sharp B1 H32 N16384 workload).
 int default_index(int pass, int d, int causal) {
   switch (pass) {
-    case 0:  // fwd: d64 Br32x4 Bc64 at three waves per SIMD (causal: Br32x8 Bc64), d96 Br32x8 Bc64, d128
-             // optimistic statistics, Br32x4 Bc64 at two waves per SIMD (causal: Bc32 at three), d192 Bc64,
-             // d256 Bc32 with optimistic statistics; causal d96 Br32x4 Bc32 at three waves per SIMD, causal
-             // d192 Bc32
+    case 0:  // fwd (opt = optimistic statistics): d64 Br32x4 Bc64 three waves per SIMD opt (causal: Br32x8
+             // Bc64 exact, which the sharp causal workload needs), d96 Br32x8 Bc64 opt (causal: Br32x4 Bc32
+             // three waves per SIMD opt), d128 Br32x4 Bc64 two waves per SIMD opt (causal: Bc32 three opt),
+             // d192 Bc64 (causal: Bc32 opt), d256 Bc32 opt
       if (d == 128) return causal ? 5 : 6;
       if (d == 256) return 2;
-      if (causal && d == 96) return 2;
-      return d == 64 ? (causal ? 2 : 4) : d == 96 ? 1 : (d == 192 && !causal) ? 1 : 0;
+      if (d == 96) return causal ? 3 : 4;
+      if (d == 192) return causal ? 3 : 1;
+      return causal ? 2 : 6;  // d == 64
     case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d192 and d256 Bk32x4 Bq32, K read from LDS; d96
              // and d128 two key blocks per wave, Bk64x4 Bq64
       return d == 64 ? 2 : d == 96 ? 3 : d == 128 ? 6 : 1;

@@ -1370,6 +1370,9 @@ const BwdConfig* dkdv_configs(int* count) {
       DKDVK_CFGV(128, 96, 64, 4), DKDVK_CFGV(256, 192, 32, 4),
       DKDVW_CFG(64, 64, 4),  DKDVW_CFG(64, 32, 4),  DKDVW_CFG(128, 64, 4), DKDVW_CFG(128, 32, 4),
       DKDVW_CFGV(128, 96, 64, 4), DKDVW_CFGV(128, 96, 32, 4),
+      // non-power-of-two workgroups: 160-224 keys (5-7 waves), 320 keys at d = 64
+      DKDVK_CFG(128, 32, 5), DKDVK_CFG(128, 32, 6), DKDV_CFG(64, 64, 5, false), DKDV_CFG(64, 64, 6, false),
+      DKDV_CFG(64, 64, 7, false), DKDV_CFG(64, 32, 10, false),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -1385,6 +1388,9 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       DKDVA_CFGV(128, 96, 64, 4, false), DKDVA_CFGV(256, 192, 32, 2, true),
       DKDVADK_CFGV(128, 96, 32, 8), DKDVADK_CFGV(256, 192, 32, 4),
       DKDVAW_CFG(64, 64, 4),  DKDVAW_CFG(64, 32, 4),  DKDVAW_CFG(128, 32, 4), DKDVAW_CFGV(128, 96, 32, 4),
+      // non-power-of-two workgroups: 160-224 keys (5-7 waves)
+      DKDVADK_CFG(128, 32, 5), DKDVADK_CFG(128, 32, 6), DKDVADK_CFG(64, 64, 5), DKDVADK_CFG(64, 64, 6),
+      DKDVADK_CFG(64, 64, 7),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -1396,6 +1402,9 @@ const BwdConfig* dq_configs(int* count) {
       DQ_CFG(128, 64, 4, 2), DQ_CFG(128, 32, 4, 2), DQ_CFG(128, 64, 8, 2),
       DQ_CFG(256, 32, 4, 1), DQ_CFG(256, 64, 4, 1),
       DQ_CFGV(128, 96, 64, 4, 2), DQ_CFGV(128, 96, 64, 8, 2), DQ_CFGV(256, 192, 32, 4, 1),
+      // non-power-of-two workgroups: 160-224 query rows (5-7 waves)
+      DQ_CFG(128, 64, 5, 2), DQ_CFG(128, 64, 6, 2), DQ_CFG(128, 64, 7, 2), DQ_CFG(64, 64, 5, 2),
+      DQ_CFG(64, 64, 6, 2),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -227,8 +227,11 @@ constexpr unsigned kOutOfRange = 0x80000000u;  // above every buffer range used 
 template <int ROWS, int W, int NW, int MODE>
 struct TileDMA {
   static constexpr int kPieces = ROWS * W * 2 / 1024;
-  static constexpr int kPerWave = kPieces / NW;
-  static_assert(kPieces % NW == 0, "tile must split into whole 1 KB pieces per wave");
+  static_assert(ROWS * W * 2 % 1024 == 0, "tile must split into whole 1 KB pieces");
+  // pieces i * NW + wave per wave; when NW does not divide kPieces (5-7 waves) the
+  // last round is issued by the waves that have a piece left (a wave-uniform test)
+  static constexpr int kPerWave = (kPieces + NW - 1) / NW;
+  static constexpr bool kEven = kPieces % NW == 0;
   unsigned off[kPerWave];
   unsigned ld;      // global row pitch, bytes
   int nvalid;       // 16-byte chunks per global row
@@ -238,6 +241,7 @@ struct TileDMA {
     const int byte = piece * 1024 + lane * 16;
     return ((byte % (2 * W)) >> 4) ^ swz<W, MODE>(byte / (2 * W));
   }
+  __device__ __forceinline__ static bool has(int i, int wave) { return kEven || i * NW + wave < kPieces; }
   // row_pitch_elems: the view's row stride (elements); head_dim: its valid columns
   __device__ __forceinline__ void init(int wave, int lane, long long row_pitch_elems, int head_dim) {
     ld = (unsigned)row_pitch_elems * 2u;
@@ -262,10 +266,12 @@ struct TileDMA {
     if (row0 + ROWS <= valid_rows) {
       const unsigned soff = __builtin_amdgcn_readfirstlane((unsigned)row0 * ld);
 #pragma unroll
-      for (int i = 0; i < kPerWave; ++i) lds_dma16(rs, off[i], soff, lds_addr(tile + (i * NW + wave) * 1024));
+      for (int i = 0; i < kPerWave; ++i)
+        if (has(i, wave)) lds_dma16(rs, off[i], soff, lds_addr(tile + (i * NW + wave) * 1024));
     } else {
 #pragma unroll
       for (int i = 0; i < kPerWave; ++i) {
+        if (!has(i, wave)) continue;
         const int piece = i * NW + wave;
         const int grow = min(row0 + piece_row(piece, lane), valid_rows - 1);
         const int ch = piece_chunk(piece, lane);

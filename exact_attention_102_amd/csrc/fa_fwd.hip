@@ -344,6 +344,10 @@ const FwdConfig* fwd_configs(int* count) {
       FWD_CFGO(128, 32, 4, 3), FWD_CFGO(64, 64, 4, 3), FWD_CFGO(64, 64, 8, 2), FWD_CFGO(256, 32, 4, 1),
       FWD_CFGVO(128, 96, 32, 4, 3), FWD_CFGVO(128, 96, 64, 8, 2), FWD_CFGVO(256, 192, 64, 4, 1),
       FWD_CFGVO(256, 192, 32, 4, 1), FWD_CFGO(128, 64, 4, 2),
+      // non-power-of-two workgroups (160, 192, 224 query rows) and the ceil(M / 4d) seed of the
+      // block-size rule (M = 160 KB of LDS: 160 keys per tile at d = 128, 320 at d = 64)
+      FWD_CFGO(128, 32, 5, 2), FWD_CFGO(128, 32, 6, 2), FWD_CFGO(128, 32, 7, 2), FWD_CFGO(128, 160, 4, 1),
+      FWD_CFG(64, 320, 2, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -1,6 +1,7 @@
 """Block-shape sweep: times every tile configuration of every kernel on one workload.
 
     python -m exact_attention_102_amd.sweep --workload b4_h16_n2048_d128 [--causal 0|1] [--d 96] [--passes 0,1,2,3]
+    python -m exact_attention_102_amd.sweep --all --jsonl OUT.jsonl --md OUT.md
 
 "Potential algorithmic improvements for backward pass" (flash-attention issue 1172)
 treats the block shape -- rows owned per workgroup x rows walked per tile, and
@@ -9,7 +10,10 @@ shapes such as 32-64 x 160-320.  This tool measures each compiled configuration
 (fa_num_configs / fa_config_name) with the same protocol as that page's benchmark
 (5 trials of 5 back-to-back dispatches; best and median reported) and prints one
 JSON record per (pass, configuration); the library's default table is set from
-these results.
+these results.  --all sweeps every head dim the library builds (64, 96, 128, 192,
+256) with both masks on B4 H16 N2048, plus the benchmark workloads at their own
+shapes, in one process, and writes the JSON records and a markdown table per
+(workload, mask, pass) with the default marked.
 """
 from __future__ import annotations
 
@@ -89,15 +93,54 @@ def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3), d_override: 
     return out
 
 
+# (workload, head dim override or 0, causal): every default of the library is chosen on one of these
+ALL_SWEEPS = [("b4_h16_n2048_d128", d, c) for d in (64, 96, 128, 192, 256) for c in (False, True)] + [
+    ("b2_h16_n8192_d128_causal", 0, True), ("b2_h16_n8192_d128_full", 0, False), ("b4_h8_n4096_d256", 0, False),
+    ("b1_h32_n16384_d64_causal_sharp", 0, True)]
+
+
+def markdown(records: list) -> str:
+    out = []
+    groups = {}
+    for r in records:
+        groups.setdefault((r["workload"], r["causal"], r["pass"]), []).append(r)
+    for (wl, causal, pas), rs in groups.items():
+        best = min(x["best_ms"] for x in rs)
+        out += ["", "### %s, %s, %s" % (wl, "causal" if causal else "non-causal", pas), "",
+                "| configuration | default | best ms | median ms | TFLOP/s (best) | vs fastest |",
+                "|---|---|---|---|---|---|"]
+        for x in rs:
+            out.append("| %s | %s | %.4f | %.4f | %.1f | %.3f |" % (x["name"], "**default**" if x["default"] else "",
+                                                                    x["best_ms"], x["median_ms"], x["tflops_best"],
+                                                                    x["best_ms"] / best))
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", default="b4_h16_n2048_d128")
     ap.add_argument("--causal", type=int, default=-1)
     ap.add_argument("--passes", default="0,1,2,3")
     ap.add_argument("--d", type=int, default=0, help="head dim in place of the workload's")
+    ap.add_argument("--all", action="store_true", help="every head dim and mask plus the benchmark workloads")
+    ap.add_argument("--jsonl", default=None)
+    ap.add_argument("--md", default=None)
     args = ap.parse_args()
-    sweep(args.workload, None if args.causal < 0 else args.causal, tuple(int(x) for x in args.passes.split(",")),
-          args.d)
+    passes = tuple(int(x) for x in args.passes.split(","))
+    if not args.all:
+        recs = sweep(args.workload, None if args.causal < 0 else args.causal, passes, args.d)
+    else:
+        recs = []
+        for wl, d, causal in ALL_SWEEPS:
+            print("# sweep %s d=%s causal=%d" % (wl, d or "-", causal), file=sys.stderr, flush=True)
+            recs += sweep(wl, int(causal), passes, d)
+    if args.jsonl:
+        with open(args.jsonl, "w") as fh:
+            for r in recs:
+                fh.write(json.dumps(r) + "\n")
+    if args.md:
+        with open(args.md, "w") as fh:
+            fh.write(markdown(recs) + "\n")
 
 
 if __name__ == "__main__":
