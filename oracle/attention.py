@@ -58,6 +58,7 @@ __all__ = [
     "attention_forward",
     "attention_backward",
     "attention_backward_jacobian",
+    "attention_backward_key_rows",
     "attention_forward_batched",
     "attention_backward_batched",
     "online_softmax_stats",
@@ -184,6 +185,43 @@ def attention_backward_jacobian(q, k, v, do, scale: float, causal: bool):
     dq = float(scale) * (ds @ k)
     dk = float(scale) * (ds.T @ q)
     return dq, dk, dv
+
+
+def attention_backward_key_rows(q, k, v, do, scale: float, causal: bool, keys, row_chunk: int = 128,
+                                workers: int | None = None):
+    """One head: dK and dV of the key rows ``keys`` only, by the chain rule of ``attention_backward``.
+
+    dV_j = sum_i P_ij dO_i and dK_j = scale * sum_i dS_ij q_i run over every query row i
+    that attends to key j; each such row's P_i is its own full max-subtracted softmax (all
+    its keys) and dS_i = P_i * (dP_i - rowsum(P_i * dP_i)) with dP_i = dO_i V^T, as in
+    ``attention_backward``.  Under the causal mask (query i sees keys j <= i) only rows
+    i >= min(keys) attend to a sampled key, so keys near the end of a long sequence need
+    few rows; without the mask every row does.  Query rows are processed in chunks on a
+    thread pool (rows are independent; the per-chunk sums only reorder fp64 additions).
+    Returns (dk [len(keys), d], dv [len(keys), d]) in fp64.
+    """
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    do = _f64(do)
+    keys = np.asarray(keys, dtype=np.int64)
+    n = q.shape[0]
+    first = int(keys.min()) if causal else 0
+    starts = list(range(first, n, row_chunk))
+
+    def part(r0):
+        r1 = min(n, r0 + row_chunk)
+        p, _ = softmax_rows(score_matrix(q[r0:r1], k, scale, causal, r0))
+        dp = do[r0:r1] @ v.T
+        ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+        return p[:, keys].T @ do[r0:r1], float(scale) * (ds[:, keys].T @ q[r0:r1])
+
+    workers = max(1, min(workers or usable_cores(), 8, len(starts)))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(part, starts))
+    dv = np.sum([a for a, _ in parts], axis=0)
+    dk = np.sum([b for _, b in parts], axis=0)
+    return dk, dv
 
 
 def _map_heads(fn, n_heads: int, workers: int | None):

@@ -2,7 +2,11 @@
 fp64 oracle on the same seeded bf16 inputs, and compare at the stated bar.
 
 Tolerances (bf16 inputs, fp32 accumulation): O max-abs <= 1e-2, LSE max-abs
-<= 1e-3, dQ/dK/dV relative L2 <= 2e-2 (relative to the oracle's norm).
+<= 1e-3, dQ/dK/dV relative L2 <= 2e-2 (relative to the oracle's norm).  Beside the
+whole-tensor figure every gradient comparison also bounds the worst single row:
+the largest per-row error norm may be at most ROW_REL of the root-mean-square row
+norm, so an error confined to a few rows (which the whole-tensor norm dilutes) still
+fails; the largest error relative to a row's own norm is reported.
 """
 from __future__ import annotations
 
@@ -19,6 +23,7 @@ O_MAX_ABS = 1e-2
 LSE_MAX_ABS = 1e-3
 GRAD_REL_L2 = 2e-2
 ZERO_GRAD_ABS = 1e-5
+ROW_REL = 5e-2
 
 
 def note(msg: str):
@@ -72,11 +77,25 @@ def check_forward(o, lse, ref_o, ref_lse, heads=None):
     return eo, el
 
 
-def check_backward(grads, refs, heads=None):
+def row_errors(g, r):
+    """(worst row error / RMS row norm, worst row error / own row norm) over the rows of the last axis."""
+    g = np.asarray(g, dtype=np.float64).reshape(-1, np.shape(g)[-1])
+    r = np.asarray(r, dtype=np.float64).reshape(-1, np.shape(r)[-1])
+    en = np.linalg.norm(g - r, axis=1)
+    rn = np.linalg.norm(r, axis=1)
+    rms = float(np.sqrt(np.mean(rn * rn)))
+    big = rn > 1e-3 * rms
+    own = float(np.max(en[big] / rn[big])) if np.any(big) else 0.0
+    return float(np.max(en)) / max(rms, 1e-300), own
+
+
+def check_backward(grads, refs, heads=None, label=""):
     errs = []
+    rows = []
     for name, g, r in zip(("dq", "dk", "dv"), grads, refs):
-        g = g.cpu().numpy().reshape(-1, *g.shape[2:])
-        r = r.reshape(-1, *r.shape[2:])
+        g = g.cpu().numpy() if hasattr(g, "cpu") else np.asarray(g)
+        g = g.reshape(-1, *g.shape[2:])
+        r = np.asarray(r).reshape(-1, *np.shape(r)[2:])
         if heads is not None:
             g, r = g[heads], r[heads]
         assert np.all(np.isfinite(g)), name + " has non-finite values"
@@ -88,7 +107,13 @@ def check_backward(grads, refs, heads=None):
         else:
             e = rel_l2(g, r)
             assert e <= GRAD_REL_L2, "%s rel-L2 error %.3e > %.0e" % (name, e, GRAD_REL_L2)
+            worst, own = row_errors(g, r)
+            assert worst <= ROW_REL, "%s worst row error %.3e of the RMS row norm > %.0e" % (name, worst, ROW_REL)
+            rows.append("%s %.1e/%.1e" % (name, worst, own))
         errs.append(e)
+    if rows:
+        note("  %srel-L2 %s; worst row (vs RMS / own norm) %s" % (label, " ".join("%.1e" % x for x in errs),
+                                                                   ", ".join(rows)))
     return errs
 
 

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 from oracle import (attention_backward, attention_backward_batched, attention_backward_jacobian,
+                    attention_backward_key_rows,
                     attention_forward, attention_forward_batched, blockwise_attention_forward,
                     online_softmax_stats, score_matrix, softmax_rows)
 
@@ -196,6 +197,50 @@ def test_gradients_match_central_differences(n, d, causal):
             fd[idx] = (lp - lm) / (2 * h)
         err = np.linalg.norm(fd - g) / np.linalg.norm(g)
         assert err <= 1e-6, err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_row_gradients_match_central_differences(causal):
+    """dK and dV of selected key rows (the large-N parity reference) against central
+    differences of L = sum(dO * O) in those rows only, on chunks smaller than the rows."""
+    n, d = 9, 4
+    q, k, v, do = rand_head(71, n, d, scale_qk=1.5)
+    scale = 0.6
+    keys = [8, 2, 5]
+    dk, dv = attention_backward_key_rows(q, k, v, do, scale, causal, keys, row_chunk=2, workers=2)
+    h = 1e-6
+    for x, g in ((k, dk), (v, dv)):
+        fd = np.zeros_like(g)
+        for a, j in enumerate(keys):
+            for c in range(d):
+                old = x[j, c]
+                x[j, c] = old + h
+                lp = loss(q, k, v, do, scale, causal)
+                x[j, c] = old - h
+                lm = loss(q, k, v, do, scale, causal)
+                x[j, c] = old
+                fd[a, c] = (lp - lm) / (2 * h)
+        err = np.linalg.norm(fd - g) / np.linalg.norm(fd)
+        assert err <= 1e-6, err
+
+
+def test_key_row_gradients_skip_rows_that_cannot_see_the_keys():
+    """Under the causal mask the key-row gradients of keys near the end use only the query
+    rows from the first sampled key on; the result must not depend on the rows before it
+    (changing them leaves the sampled dK, dV unchanged) and matches the full backward's."""
+    n, d = 40, 6
+    q, k, v, do = rand_head(72, n, d)
+    keys = [39, 37, 31]
+    dk, dv = attention_backward_key_rows(q, k, v, do, 0.4, True, keys, row_chunk=7)
+    q2, do2 = q.copy(), do.copy()
+    q2[:31] += 3.0
+    do2[:31] *= -2.0
+    dk2, dv2 = attention_backward_key_rows(q2, k, v, do2, 0.4, True, keys, row_chunk=5)
+    np.testing.assert_allclose(dk2, dk, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dv2, dv, rtol=1e-12, atol=1e-13)
+    _, fk, fv = attention_backward(q, k, v, do, 0.4, True)
+    np.testing.assert_allclose(dk, fk[keys], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, fv[keys], rtol=1e-10, atol=1e-12)
 
 
 @pytest.mark.parametrize("causal", [False, True])
