@@ -360,7 +360,7 @@ def _dropout_arg(dropout):
 
 def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, workspace=None, stream=None,
                    dropout=None):
-    """Forward for any head dim 1..256 and strided [B, H, N, d] views (e.g. a [B, N, H, d] tensor
+    """Forward for any head dim 1..384 and strided [B, H, N, d] views (e.g. a [B, N, H, d] tensor
     transposed); returns (o, lse).  o defaults to a new contiguous fp32 tensor.  dropout = (p, seed,
     offset) runs fa_fwd_general_dropout."""
     torch = _torch()
@@ -388,7 +388,7 @@ def fa_fwd_general(q, k, v, causal: bool, scale: float, o=None, lse=None, worksp
 
 def fa_bwd_general(q, k, v, o, lse, dout, causal: bool, scale: float, variant: int = FA_BWD_7GEMM,
                    dq=None, dk=None, dv=None, workspace=None, stream=None, dropout=None):
-    """Backward for any head dim 1..256 and strided views; returns (dq, dk, dv) (new contiguous fp32
+    """Backward for any head dim 1..384 and strided views; returns (dq, dk, dv) (new contiguous fp32
     tensors unless given).  dropout = the forward's (p, seed, offset) runs fa_bwd_general_dropout."""
     torch = _torch()
     B, H, N, d = q.shape

@@ -31,8 +31,11 @@ bool overlaps(Range a, Range b) {
 
 Range rng(const void* p, size_t bytes) { return Range{static_cast<const char*>(p), bytes}; }
 
-// Head dims with kernels of their own (96 and 192 on 128- and 256-wide tiles).
-bool supported_d(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
+// Head dims with kernels of their own (96 and 192 on 128- and 256-wide tiles, 288, 320, 352
+// and 384 on 384-wide tiles).
+bool supported_d(int d) {
+  return d == 64 || d == 96 || d == 128 || d == 192 || d == 256 || d == 288 || d == 320 || d == 352 || d == 384;
+}
 
 // Shared size checks: positive sizes, 32-bit grid and row counts, 64-bit byte counts.
 // One head of a bf16 input (N * d * 2 bytes) must stay below 2^31 bytes: the tile
@@ -85,6 +88,7 @@ int count_for_d(const Cfg* t, int n, int d) {
 // configurations for that d.  Where the shapes disagree, the benchmark workload of that
 // head dim decides (d64 causal: the sharp B1 H32 N16384 workload).
 int default_index(int pass, int d, int causal) {
+  if (d > 256) return pass >= 0 && pass <= 3 ? 0 : -1;  // one configuration per pass above 256
   switch (pass) {
     case 0:  // fwd (opt = optimistic statistics): d64 Br32x4 Bc64 three waves per SIMD opt (causal: Br32x8
              // Bc64 exact, which the sharp causal workload needs), d96 Br32x8 Bc64 opt (causal: Br32x4 Bc32
@@ -582,9 +586,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const float* o, co
 // views directly, otherwise through zero-padded contiguous copies.
 namespace {
 
-constexpr int kMaxGeneralD = 256;
+constexpr int kMaxGeneralD = 384;
 
-int padded_d(int d) { return d <= 64 ? 64 : (d <= 96 ? 96 : (d <= 128 ? 128 : (d <= 192 ? 192 : 256))); }
+int padded_d(int d) {
+  if (d > 256) return (d + 31) / 32 * 32;  // 288, 320, 352, 384
+  return d <= 64 ? 64 : (d <= 96 ? 96 : (d <= 128 ? 128 : (d <= 192 ? 192 : 256)));
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -656,6 +663,7 @@ fa_status fwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   const fa_status sz = check_general(B, H, N, d, scale);
   if (sz != FA_OK) return sz;
+  if (drop && drop->t != 0 && d > 256) return FA_ERR_UNSUPPORTED;  // no dropout kernels above 256
   const fa_strides strs[] = {q_str, k_str, v_str, o_str};
   for (const fa_strides& t : strs)
     if (!strides_ok(t)) return FA_ERR_INVALID_ARG;
@@ -743,6 +751,7 @@ fa_status bwd_general_impl(const void* q, fa_strides q_str, const void* k, fa_st
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
   const fa_status sz = check_general(B, H, N, d, scale);
   if (sz != FA_OK) return sz;
+  if (drop && drop->t != 0 && d > 256) return FA_ERR_UNSUPPORTED;  // no dropout kernels above 256
   if (variant != FA_BWD_5GEMM_ATOMIC && variant != FA_BWD_7GEMM) return FA_ERR_UNSUPPORTED;
   const fa_strides strs[] = {q_str, k_str, v_str, o_str, dout_str, dq_str, dk_str, dv_str};
   for (const fa_strides& t : strs)

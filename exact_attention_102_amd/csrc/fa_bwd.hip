@@ -71,14 +71,16 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PreArgs a) {
 }
 
 int launch_preprocess(const PreArgs& a, int d, hipStream_t stream) {
-  // head dims 96 and 192 run on the 128- and 256-wide row kernels (a.hd masks the rest)
-  const int kd = d == 96 ? 128 : (d == 192 ? 256 : d);
+  // head dims 96 and 192 run on the 128- and 256-wide row kernels, 288..384 on the 512-wide one
+  // (a.hd masks the rest)
+  const int kd = d == 96 ? 128 : (d == 192 ? 256 : (d > 256 ? 512 : d));
   const int rpb = 256 / (kd / 8);
   const int blocks = (a.rows + rpb - 1) / rpb;
   switch (kd) {
     case 64: hipLaunchKernelGGL(preprocess_kernel<64>, dim3(blocks), dim3(256), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(preprocess_kernel<128>, dim3(blocks), dim3(256), 0, stream, a); break;
     case 256: hipLaunchKernelGGL(preprocess_kernel<256>, dim3(blocks), dim3(256), 0, stream, a); break;
+    case 512: hipLaunchKernelGGL(preprocess_kernel<512>, dim3(blocks), dim3(256), 0, stream, a); break;
     default: return -1;
   }
   return 0;
@@ -1223,6 +1225,269 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV for head dims above 256 (tiles D = 384 wide, DV = 288 .. 384 computed columns).
+// For 32 keys per wave, the dK^T/dV^T accumulators of all DV columns (DV registers per
+// lane) plus the K and V fragments of the S = Q K^T and dP = dO V^T products (DV / 4
+// each) exceed the register file, and K/V tiles in LDS next to the double-buffered Q/dO
+// tiles exceed 160 KB.  So each workgroup accumulates one window of WIN = 128 columns
+// (three workgroups per key tile): it recomputes S and dP over the full DV contraction (K
+// and V in registers) and runs the dV/dK products, the stores and, ATOMIC (5-GEMM), the
+// dQ product only for its window.  S and dP are therefore computed once per window -- the
+// recompute-for-capacity trade that issue 1172 describes for large head dims, where the
+// accumulators no longer fit (192-column windows, two per key tile, spill 90-340
+// registers).  ATOMIC: dQ[:, window] = dS K[:, window] with the window's K columns in an
+// LDS tile, one fp32 atomic per dq element and window.
+template <int D, int DV, int WIN, int BQ, int NW, bool CAUSAL, bool ATOMIC>
+__global__ __launch_bounds__(NW * 64, 1) void dkdv_split_kernel(BwdArgs a) {
+  constexpr int BK = 32 * NW, QBN = BQ / 32, KK = DV / 16, DBW = WIN / 32;
+  constexpr int NSPLIT = (DV + WIN - 1) / WIN;
+  constexpr int NT = NW * 64;
+  constexpr int QTILE = BQ * D * 2;
+  constexpr int KW_BYTES = ATOMIC ? BK * WIN * 2 : 16;
+  constexpr int DST_BYTES = ATOMIC ? BK * BQ * 2 : 16;
+  static_assert(WIN % 128 == 0 && D == 384, "column windows are multiples of 128 on 384-wide tiles");
+  // Q tiles in slots 0-1 and dO tiles in slots 2-3 of one array, the statistics of the two
+  // query tiles in one array: buffers are picked by computed offsets, never through a table
+  // of LDS pointers (which hides the accesses from the compiler's LDS allocation)
+  __shared__ __attribute__((aligned(1024))) char qds[4 * QTILE];
+  __shared__ __attribute__((aligned(16))) float sts[4 * BQ];
+  __shared__ __attribute__((aligned(1024))) char kws[KW_BYTES];
+  __shared__ __attribute__((aligned(1024))) char dsts[DST_BYTES];
+  auto qbuf = [&](int i) { return (LDS char*)qds + i * QTILE; };
+  auto dbuf = [&](int i) { return (LDS char*)qds + (2 + i) * QTILE; };
+  auto stb = [&](int i) { return (LDS float*)sts + i * 2 * BQ; };
+  LDS char* const kwin = (LDS char*)kws;
+  LDS char* const dst = (LDS char*)dsts;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int N = a.N;
+  const int nkt = (N + BK - 1) / BK;
+  const int split = blockIdx.x % NSPLIT;
+  int bh, kt;
+  if (CAUSAL) {
+    causal_order(blockIdx.x / NSPLIT, a.B * a.H, nkt, false, bh, kt);
+  } else {
+    const int item = xcd_remap(blockIdx.x / NSPLIT, a.B * a.H * nkt);
+    bh = item / nkt;
+    kt = item % nkt;
+  }
+  const int c0 = split * WIN;                       // the window's first column
+  const int dbv = min(DBW, (DV - c0) / 32);         // 32-column blocks of the window inside DV
+  const __bf16* Qh = a.q + head_base(a.vq, bh, a.H);
+  const __bf16* Kh = a.k + head_base(a.vk, bh, a.H);
+  const __bf16* Vh = a.v + head_base(a.vv, bh, a.H);
+  const __bf16* dOh = a.dout + head_base(a.vdo, bh, a.H);
+  const float* lseh = a.lse + (size_t)bh * N;
+  const float* delh = a.delta + (size_t)bh * N;
+  float* dqh = ATOMIC ? a.dq + (size_t)bh * N * DV : nullptr;
+  const int hd = a.hd;
+  const float c = a.scale * kLog2e;
+
+  const int k0 = kt * BK;
+  const int kw = k0 + wave * 32;
+  const int key = kw + l32;
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? k0 / BQ : 0;
+  TileDMA<BQ, D, NW, kBoth> qdma;
+  qdma.init(wave, lane, a.vq.sn, hd);
+  qdma.issue(Qh, qt0 * BQ, N, qbuf(0), wave, lane);
+  qdma.issue(dOh, qt0 * BQ, N, dbuf(0), wave, lane);
+  if constexpr (ATOMIC) {  // the window's K columns of the workgroup's keys (transposed reads)
+    TileDMA<BK, WIN, NW, kColOnly> kd;
+    kd.init(wave, lane, a.vk.sn, min(WIN, hd - c0));
+    kd.issue(Kh + c0, k0, N, kwin, wave, lane);
+  }
+  RowStager<BQ, NT> srow;
+  srow.load(lseh, delh, qt0 * BQ, N, tid);
+  srow.store(stb(0), N, tid);
+
+  bf16x8 kf[KK], vf[KK];
+  {
+    const int krow = min(key, N - 1);  // keys past the end: masked below, never stored
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      kf[kk] = load_row_chunk(Kh + (size_t)krow * a.vk.sn, 2 * kk + g, hd >> 3);
+      vf[kk] = load_row_chunk(Vh + (size_t)krow * a.vv.sn, 2 * kk + g, hd >> 3);
+    }
+  }
+  f32x16 dk[DBW], dv[DBW];
+#pragma unroll
+  for (int db = 0; db < DBW; ++db) {
+    dk[db] = zero16();
+    dv[db] = zero16();
+  }
+  RowOffsets<D, kBoth> fr;
+  fr.init(lane);
+  ColOffsets<D, kBoth> fc;
+  fc.init(lane, c0 / 32);
+
+  wait_tile();
+  __syncthreads();
+  for (int it = qt0; it < nqt; ++it) {
+    const int cur = (it - qt0) & 1;
+    fr.refresh();
+    fc.refresh();
+    qdma.refresh();
+    if (it + 1 < nqt) {
+      qdma.issue(Qh, (it + 1) * BQ, N, qbuf(cur ^ 1), wave, lane);
+      qdma.issue(dOh, (it + 1) * BQ, N, dbuf(cur ^ 1), wave, lane);
+      srow.load(lseh, delh, (it + 1) * BQ, N, tid);
+    }
+    const LDS char* qtl = qbuf(cur);
+    const LDS char* dotl = dbuf(cur);
+    const LDS float* l2t = stb(cur);
+    const LDS float* dlt = stb(cur) + BQ;
+    const int q0 = it * BQ;
+#pragma unroll
+    for (int qb = 0; qb < QBN; ++qb) {
+      const int qbase = q0 + qb * 32;
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 sb0, sb1;
+      if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
+        f32x16 sc = zero16(), dp = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          sc = mfma32(fr.row(qtl, qb * 32, kk), kf[kk], sc);
+          dp = mfma32(fr.row(dotl, qb * 32, kk), vf[kk], dp);
+          fence_every<4>(kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float l2[16], dl[16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int r = qb * 32 + 16 * h + 8 * g + 4 * hf;
+            const f32x4 lv = *(const LDS f32x4*)(l2t + r);
+            const f32x4 dd = *(const LDS f32x4*)(dlt + r);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              l2[8 * h + 4 * hf + e] = lv[e];
+              dl[8 * h + 4 * hf + e] = dd[e];
+            }
+          }
+        }
+        // queries past the end have lse2 = +inf (P = 0); causal: keys after the query score -inf
+        if (CAUSAL && qbase < kw + 31) {
+          asm volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int q = qbase + 16 * (r >> 3) + 8 * g + (r & 7);
+            if (key > q) sc[r] = -INFINITY;
+          }
+        }
+        f32x16 p, ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = exp2_hw(fmaf(sc[r], c, -l2[r]));
+          p[r] = pv;
+          ds[r] = pv * (dp[r] - dl[r]);
+        }
+        const bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
+        sb0 = pack8(ds, 0);
+        sb1 = pack8(ds, 8);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < DBW; ++db) {
+          if (db < dbv) {
+            dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
+            dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+          }
+          fence_every<2>(db);
+        }
+        if (!CAUSAL && key >= N) {  // clamped key rows must not reach dQ
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            sb0[e] = (__bf16)0.f;
+            sb1[e] = (__bf16)0.f;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sb0[e] = (__bf16)0.f;
+          sb1[e] = (__bf16)0.f;
+        }
+      }
+      if constexpr (ATOMIC) {
+        *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 8 * g)) = sb0;
+        *(LDS bf16x8*)(dst + tile_off<BQ, kBoth>(wave * 32 + l32, qb * 32 + 16 + 8 * g)) = sb1;
+      }
+    }
+    if constexpr (ATOMIC) {
+      // dQ[q0 .., window] = dS K[keys, window]: the waves split the (query block, d block) pairs
+      __syncthreads();
+      for (int t = wave; t < QBN * DBW; t += NW) {
+        const int qb = t / DBW, db = t % DBW;
+        if (db >= dbv) continue;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+          acc = mfma32(ColOffsets<BQ, kBoth>::col_dyn(dst, ks * 16, qb, lane),
+                       ColOffsets<WIN, kColOnly>::col_dyn(kwin, ks * 16, db, lane), acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = q0 + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (q < N) unsafeAtomicAdd(dqh + (size_t)q * DV + c0 + db * 32 + l32, acc[r] * a.scale);
+        }
+      }
+    }
+    wait_tile();
+    if (it + 1 < nqt) srow.store(stb(cur ^ 1), N, tid);
+    __syncthreads();
+    // The last dK/dV products sit in a branch (db < dbv) at the end of the body; on the
+    // loop-exit path the compiler leaves 10 of the 12 wait states between that MFMA and the
+    // first read of its accumulators (the register copies it places at the loop exit, ahead
+    // of anything written after the loop).  Eight more at the end of every iteration.
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  if (key < N) {
+    float* dkr = a.dk + head_base(a.vdk, bh, a.H) + (size_t)key * a.vdk.sn;
+    float* dvr = a.dv + head_base(a.vdv, bh, a.H) + (size_t)key * a.vdv.sn;
+#pragma unroll
+    for (int db = 0; db < DBW; ++db) {
+      if (db >= dbv) continue;
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int col = c0 + db * 32 + 8 * a4 + 4 * g;
+        const f32x4 kv = {dk[db][4 * a4] * a.scale, dk[db][4 * a4 + 1] * a.scale, dk[db][4 * a4 + 2] * a.scale,
+                          dk[db][4 * a4 + 3] * a.scale};
+        const f32x4 vv = {dv[db][4 * a4], dv[db][4 * a4 + 1], dv[db][4 * a4 + 2], dv[db][4 * a4 + 3]};
+        if (col < hd) {
+          *(f32x4*)(dkr + col) = kv;
+          *(f32x4*)(dvr + col) = vv;
+        }
+      }
+    }
+  }
+}
+
+template <int D, int DV, int WIN, int BQ, int NW, bool ATOMIC>
+static int launch_dkdv_split(const BwdArgs& a, bool causal, hipStream_t stream) {
+  constexpr int BK = 32 * NW, NSPLIT = (DV + WIN - 1) / WIN;
+  const int nkt = (a.N + BK - 1) / BK;
+  const long long blocks = (long long)a.B * a.H * nkt * NSPLIT;
+  if (blocks <= 0 || blocks > 0x7fffffff) return -1;
+  if (a.drop_t != 0) return -1;
+  if (causal) {
+    hipLaunchKernelGGL((dkdv_split_kernel<D, DV, WIN, BQ, NW, true, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64), 0,
+                       stream, a);
+  } else {
+    hipLaunchKernelGGL((dkdv_split_kernel<D, DV, WIN, BQ, NW, false, ATOMIC>), dim3((unsigned)blocks), dim3(NW * 64),
+                       0, stream, a);
+  }
+  return 0;
+}
+
+// ---------------------------------------------------------------------------
 template <int D, int DV, int BQ, int NW, bool ATOMIC, int KVL, bool DEFER = false, bool DROP = false>
 static int launch_dkdv(const BwdArgs& a, bool causal, hipStream_t stream) {
   constexpr int BK = 32 * NW;
@@ -1353,6 +1618,16 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
     DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #DV " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " defer" #DEF, \
         &launch_dkdv<D, DV, BQ, NW, true, KVL, DEF, true>                                                  \
   }
+// head dims above 256: 384-wide tiles, three 128-column windows per key tile
+#define DKDVS_CFG(DV)                                                                                    \
+  {                                                                                                        \
+    DV, 128, 32, 4, "dkdv d" #DV " (tiles 384) Bk32x4 Bq32 kv_regs split128", &launch_dkdv_split<384, DV, 128, 32, 4, false> \
+  }
+#define DKDVAS_CFG(DV)                                                                                   \
+  {                                                                                                        \
+    DV, 128, 32, 4, "dkdv+atomic-dq d" #DV " (tiles 384) Bk32x4 Bq32 kv_regs split128",                   \
+        &launch_dkdv_split<384, DV, 128, 32, 4, true>                                                      \
+  }
 #define DQ_DROP_CFG(D, DV, BC, NW, OCC)                                                                 \
   {                                                                                                        \
     DV, 32 * (NW), BC, NW, "dq+dropout d" #DV " Bq32x" #NW " Bc" #BC " occ" #OCC,                         \
@@ -1373,6 +1648,7 @@ const BwdConfig* dkdv_configs(int* count) {
       // non-power-of-two workgroups: 160-224 keys (5-7 waves), 320 keys at d = 64
       DKDVK_CFG(128, 32, 5), DKDVK_CFG(128, 32, 6), DKDV_CFG(64, 64, 5, false), DKDV_CFG(64, 64, 6, false),
       DKDV_CFG(64, 64, 7, false), DKDV_CFG(64, 32, 10, false),
+      DKDVS_CFG(288), DKDVS_CFG(320), DKDVS_CFG(352), DKDVS_CFG(384),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -1391,6 +1667,7 @@ const BwdConfig* dkdv_atomic_configs(int* count) {
       // non-power-of-two workgroups: 160-224 keys (5-7 waves)
       DKDVADK_CFG(128, 32, 5), DKDVADK_CFG(128, 32, 6), DKDVADK_CFG(64, 64, 5), DKDVADK_CFG(64, 64, 6),
       DKDVADK_CFG(64, 64, 7),
+      DKDVAS_CFG(288), DKDVAS_CFG(320), DKDVAS_CFG(352), DKDVAS_CFG(384),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
@@ -1405,6 +1682,8 @@ const BwdConfig* dq_configs(int* count) {
       // non-power-of-two workgroups: 160-224 query rows (5-7 waves)
       DQ_CFG(128, 64, 5, 2), DQ_CFG(128, 64, 6, 2), DQ_CFG(128, 64, 7, 2), DQ_CFG(64, 64, 5, 2),
       DQ_CFG(64, 64, 6, 2),
+      DQ_CFGV(384, 288, 32, 4, 1), DQ_CFGV(384, 320, 32, 4, 1), DQ_CFGV(384, 352, 32, 4, 1),
+      DQ_CFGV(384, 384, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -67,6 +67,8 @@ __device__ __forceinline__ int pi_row(int R) {
 //            fragments 2-way at worst.
 // W = 64 packs two rows per 256-byte bank line and uses the analogous bits on r / 2;
 // W = 32 (only the dS^T tile, written by rows and read transposed) uses 2 ((r/8)%2).
+// Wider tiles (W a multiple of 128, up to 384) use the W >= 128 patterns on every group
+// of 16 chunks.
 // Every transposed-readable variant satisfies swz(r + 4) == swz(r) for r % 8 < 4,
 // so a transposed fragment's second read (4 rows further down) reuses the first
 // read's lane offset, and every variant depends only on r % 16.
@@ -132,9 +134,10 @@ struct ColOffsets {
     const int ccol = (((lane >> 4) & 1) << 4) + ((lane & 3) << 2);
     return tile_off<W, MODE>(crow, db * 32 + ccol);
   }
-  __device__ __forceinline__ void init(int lane) {
+  // cb0: a first 32-column block (a column window); col(.., db) then reads block cb0 + db
+  __device__ __forceinline__ void init(int lane, int cb0 = 0) {
 #pragma unroll
-    for (int db = 0; db < NC; ++db) cf[db] = lane_off(lane, db);
+    for (int db = 0; db < NC; ++db) cf[db] = lane_off(lane, cb0 + db);
   }
   __device__ __forceinline__ void refresh() {
 #pragma unroll

@@ -348,6 +348,9 @@ const FwdConfig* fwd_configs(int* count) {
       // block-size rule (M = 160 KB of LDS: 160 keys per tile at d = 128, 320 at d = 64)
       FWD_CFGO(128, 32, 5, 2), FWD_CFGO(128, 32, 6, 2), FWD_CFGO(128, 32, 7, 2), FWD_CFGO(128, 160, 4, 1),
       FWD_CFG(64, 320, 2, 1),
+      // head dims above 256 on 384-wide tiles
+      FWD_CFGVO(384, 288, 32, 4, 1), FWD_CFGVO(384, 320, 32, 4, 1), FWD_CFGVO(384, 352, 32, 4, 1),
+      FWD_CFGVO(384, 384, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

@@ -6,15 +6,16 @@ for backward pass" (4..96 step 4, ..160 step 8, ..256 step 16, ..384 step 32).
 
 Each point runs the general entry points on seeded N(0,1) bf16 inputs (the first D
 columns of one draw), non-causal: head dims other than the built 64/96/128/192/256
-run on the kernels of the next built size, padded inside the kernels when D is a
+and 288/320/352/384 run on the kernels of the next built size, padded inside the kernels when D is a
 multiple of 8 and through zero-padded copies otherwise,
 with that page's protocol: 5 trials of 5 back-to-back dispatches, best trial.  It
 reports TFLOP/s credited with the true head dim (4D flop per pair forward, 10D for
 both backward designs), the page's instruction rates ((2D+5) N^2 forward, (3D+5)
 N^2 + (4D+5) N^2 for the backward kernels, in G per second), and which backward
 design is faster -- the page expects the answer to depend on head dim and chip.
-Head dims above 256 are not built (the accumulators do not fit the register file
-at one workgroup per CU) and are listed as such.
+Above 256 the dK/dV accumulators of all columns no longer fit the register file, so
+the dK/dV pass runs one 128-column window per workgroup and recomputes S and dP for
+each window (three windows at 384); the forward holds Q and O for all columns.
 """
 from __future__ import annotations
 
@@ -28,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK = 2500.0
+BUILT = (64, 96, 128, 192, 256, 288, 320, 352, 384)
 
 
 def main():
@@ -53,11 +55,11 @@ def main():
         raise SystemExit("dspectrum needs a GPU")
     B, H, N = args.B, args.H, args.N
     # one seeded draw at the widest built head dim; each point uses its first D columns
-    full = [workloads.to_bf16(x).cuda() for x in workloads.draw(B, H, N, 256, args.seed)]
+    full = [workloads.to_bf16(x).cuda() for x in workloads.draw(B, H, N, BUILT[-1], args.seed)]
     rows = []
     for D in d_spectrum():
         rec = {"D": D, "B": B, "H": H, "N": N}
-        if D > 256:
+        if D > BUILT[-1]:
             rec["supported"] = False
             rows.append(rec)
             print(json.dumps(rec), flush=True)
@@ -86,7 +88,7 @@ def main():
         t_5, _ = time_calls(bwd(FA_BWD_5GEMM_ATOMIC), torch)
         t_7, _ = time_calls(bwd(FA_BWD_7GEMM), torch)
         rec.update({
-            "supported": True, "padded_to": min(b for b in (64, 96, 128, 192, 256) if b >= D),
+            "supported": True, "padded_to": min(b for b in BUILT if b >= D),
             "fwd_ms": round(t_f, 4), "bwd5_ms": round(t_5, 4), "bwd7_ms": round(t_7, 4),
             "fwd_tflops": round(fl["fwd"] / t_f / 1e9, 1),
             "bwd5_tflops": round(fl["bwd_effective"] / t_5 / 1e9, 1),
@@ -108,7 +110,7 @@ def main():
             fh.write("Best of 5 trials x 5 dispatches.  TFLOP/s credit the true head dim D: 4D (fwd) and 10D (both "
                      "backward designs) flop per pair, peak 2500.  G instr/s: the page's (2D+5) N^2 for the forward "
                      "and (3D+5) N^2 + (4D+5) N^2 for the 7-GEMM backward's two kernels.  Head dims other than "
-                     "64/96/128/192/256 run on the kernels of the next built size (`padded`): padded inside the kernels "
+                     "64/96/128/192/256/288/320/352/384 run on the kernels of the next built size (`padded`): padded inside the kernels "
                      "when D is a multiple of 8, through zero-padded copies otherwise.\n\n")
             fh.write("| D | padded | fwd TF | 5-GEMM bwd TF | 7-GEMM bwd TF | fwd G instr/s | 7-GEMM bwd G instr/s | "
                      "t7/t5 | faster bwd |\n|---|---|---|---|---|---|---|---|---|\n")

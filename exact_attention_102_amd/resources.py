@@ -33,6 +33,7 @@ PARAMS = {
     "fwd_kernel": ["D", "DV", "BC", "NW", "OCC", "CAUSAL", "DROP", "OPT"],
     "dkdv_kernel": ["D", "DV", "BQ", "NW", "CAUSAL", "ATOMIC", "KVL", "DEFER", "DROP"],
     "dkdv_wide_kernel": ["D", "DV", "BQ", "NW", "CAUSAL", "ATOMIC"],
+    "dkdv_split_kernel": ["D", "DV", "WIN", "BQ", "NW", "CAUSAL", "ATOMIC"],
     "dq_kernel": ["D", "DV", "BC", "NW", "OCC", "CAUSAL", "DROP"],
     "preprocess_kernel": ["D"],
 }
@@ -62,6 +63,9 @@ def describe(kind: str, p: dict) -> str:
             " +dropout" if p["DROP"] else "")
     if kind == "dkdv_wide_kernel":
         return "dkdv%s d%d%s Bk64x%d Bq%d wide" % ("+atomic-dq" if p["ATOMIC"] else "", d, tiles, p["NW"], p["BQ"])
+    if kind == "dkdv_split_kernel":
+        return "dkdv%s d%d%s Bk32x%d Bq%d kv_regs split%d" % ("+atomic-dq" if p["ATOMIC"] else "", d, tiles, p["NW"],
+                                                              p["BQ"], p["WIN"])
     if kind == "dkdv_kernel":
         kvl = {0: "kv_regs", 1: "kv_lds", 2: "k_lds"}[p["KVL"]]
         return "dkdv%s d%d%s Bk32x%d Bq%d %s%s%s" % ("+atomic-dq" if p["ATOMIC"] else "", d, tiles, p["NW"], p["BQ"],

@@ -84,21 +84,21 @@ def classify(name: str):
     if not m:
         return None
     kind, targs = m.group(1), [t.strip() for t in m.group(2).split(",")]
-    # template arguments: fwd / dq <D, DV, tile, waves, occupancy, CAUSAL, DROP>;
-    # dkdv <D, DV, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>; dkdv_wide <D, DV, BQ, waves, CAUSAL, ATOMIC>;
+    # template arguments: fwd <D, DV, tile, waves, occupancy, CAUSAL, DROP, OPT>; dq <D, DV, tile, waves,
+    # occupancy, CAUSAL, DROP>; dkdv <D, DV, BQ, waves, CAUSAL, ATOMIC, KV_LDS, DEFER, DROP>;
+    # dkdv_wide <D, DV, BQ, waves, CAUSAL, ATOMIC>; dkdv_split <D, DV, window, BQ, waves, CAUSAL, ATOMIC>;
     # dropout kernels are not classified
-    if targs[-1] == "true" and kind in ("fwd", "dq", "dkdv"):
+    flag = lambda i: i < len(targs) and targs[i] == "true"  # noqa: E731
+    if (kind in ("fwd", "dq") and flag(6)) or (kind == "dkdv" and flag(8)):
         return None
-    if kind == "dkdv_wide":
-        causal, atomic = targs[4] == "true", targs[5] == "true"
+    if kind in ("dkdv_wide", "dkdv"):
+        causal, atomic = flag(4), flag(5)
         return ("dkdv_atomic" if atomic else "dkdv"), ("causal" if causal else "full")
-    if kind == "fwd":
-        return "fwd", ("causal" if targs[5] == "true" else "full")
-    if kind == "dq":
-        return "dq", ("causal" if targs[5] == "true" else "full")
-    if kind == "dkdv":
-        causal, atomic = targs[4] == "true", targs[5] == "true"
+    if kind == "dkdv_split":
+        causal, atomic = flag(5), flag(6)
         return ("dkdv_atomic" if atomic else "dkdv"), ("causal" if causal else "full")
+    if kind in ("fwd", "dq"):
+        return kind, ("causal" if flag(5) else "full")
     if kind == "preprocess":
         return "preprocess", None
     return None

@@ -33,8 +33,8 @@
  *             nothing is launched and outputs are untouched.  FA_ERR_INVALID_ARG:
  *             null/misaligned pointer, B, H or N <= 0, non-finite or non-positive
  *             scale, aliasing, or a tensor too large for 32-bit in-head indexing;
- *             FA_ERR_UNSUPPORTED: head dim not in {64, 96, 128, 192, 256} or unknown
- *             variant/config; FA_ERR_WORKSPACE: workspace missing or too small;
+ *             FA_ERR_UNSUPPORTED: head dim not in {64, 96, 128, 192, 256, 288, 320, 352,
+ *             384} or unknown variant/config; FA_ERR_WORKSPACE: workspace missing or too small;
  *             FA_ERR_HIP: a launch failed (hipGetLastError after the launch);
  *             FA_ERR_TOO_LARGE: the problem exceeds the fixed scratch of
  *             fa_bwd_noalloc.
@@ -157,7 +157,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
                     size_t workspace_bytes, void* stream, int cfg_dkdv, int cfg_dq);
 
 /* ---------------------------------------------------------------------------
- * General entry points: any head dimension 1 <= d <= 256 and strided views.
+ * General entry points: any head dimension 1 <= d <= 384 and strided views.
  *
  * Every [B,H,N,d] tensor is described by its base pointer and element strides
  * (b, h, n): element (b, h, n, i) is at base[b*stride.b + h*stride.h + n*stride.n + i]
@@ -166,7 +166,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
  * lse 16 bytes).  The math is that of fa_fwd / fa_bwd; the pages' kernels are
  * built for fixed head dimensions, and issue 1172 asks for arbitrary head
  * dimensions with strided rows.  The fused kernels run at Dp = the smallest of 64,
- * 96, 128, 192, 256 that is >= d, with columns d .. Dp-1 taken as zeros (zero columns change
+ * 96, 128, 192, 256 that is >= d, or above 256 d rounded up to a multiple of 32, with columns d .. Dp-1 taken as zeros (zero columns change
  * no score, so the result is the attention of the d columns):
  *   - in place, reading and writing the caller's views directly, when d is a
  *     multiple of 8, every base pointer is 16-byte aligned, every stride is a
@@ -178,7 +178,8 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const float* o,
  *   - otherwise through zero-padded contiguous copies held in the workspace,
  *     whose results' first d columns are written into the caller's views.
  * Validation and errors as above; views that overlap an output are rejected
- * (FA_ERR_INVALID_ARG), d outside 1..256 is FA_ERR_UNSUPPORTED. */
+ * (FA_ERR_INVALID_ARG), d outside 1..384 is FA_ERR_UNSUPPORTED (with dropout, d above
+ * 256 as well). */
 typedef struct {
   long long b, h, n;
 } fa_strides;
@@ -220,7 +221,8 @@ fa_status fa_bwd_general(const void* q, fa_strides q_str, const void* k, fa_stri
  * the backward gives the gradients of sum(dout * o) for that same mask, redrawn
  * from (seed, offset): pass the forward's values.  A p that rounds to t = 0 runs the
  * plain kernels.  Head dims 64, 96, 128, 192, 256 here (any d in 1..256 through the general
- * dropout entries below); each pass runs one tile shape per head dim.
+ * dropout entries below; above 256 dropout is FA_ERR_UNSUPPORTED); each pass runs one tile
+ * shape per head dim.
  * Errors as above; p outside [0, 1) or not finite is FA_ERR_INVALID_ARG. */
 typedef struct {
   double p;                /* drop probability, 0 <= p < 1                           */

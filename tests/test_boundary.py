@@ -51,7 +51,7 @@ def test_status_strings_and_version(L):
 def test_config_tables(L):
     from exact_attention_102_amd import fa_config_name, fa_default_config, fa_num_configs
     for p in range(4):
-        for d in (64, 128, 256):
+        for d in (64, 128, 256, 288, 384):
             n = fa_num_configs(p, d)
             assert n >= 1
             names = [fa_config_name(p, d, False, i) for i in range(n)]
@@ -126,7 +126,7 @@ def test_heads_of_2gib_or_more_rejected(L):
     address a head through one 32-bit buffer range and zero-fill the padded columns of
     d = 96 / 192 through an offset of 2^31, which must fall outside that range."""
     from exact_attention_102_amd import FA_ERR_INVALID_ARG
-    for d in (64, 96, 128, 192, 256):
+    for d in (64, 96, 128, 192, 256, 288, 384):
         n_limit = -(-(1 << 31) // (2 * d))       # smallest N with N * d * 2 >= 2^31
         assert fwd(L, N=n_limit, d=d) == FA_ERR_INVALID_ARG
         assert bwd(L, N=n_limit, d=d, ws_bytes=1 << 40) == FA_ERR_INVALID_ARG
@@ -204,7 +204,7 @@ def test_report_tile_counts_match_brute_force():
 
 
 def test_general_entries_validate_before_launching(L):
-    """Any head dim 1..256 and strided views: sizes of the padded workspace and the error paths (no
+    """Any head dim 1..384 and strided views: sizes of the padded workspace and the error paths (no
     call here reaches a launch)."""
     from exact_attention_102_amd import FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE
     from exact_attention_102_amd.binding import FaStrides
@@ -213,12 +213,13 @@ def test_general_entries_validate_before_launching(L):
         return (x + 255) // 256 * 256
 
     B, H, N = 2, 3, 77
-    for d, dp in ((1, 64), (40, 64), (64, 64), (65, 96), (96, 96), (127, 128), (160, 192), (192, 192), (256, 256)):
+    for d, dp in ((1, 64), (40, 64), (64, 64), (65, 96), (96, 96), (127, 128), (160, 192), (192, 192), (256, 256),
+                  (257, 288), (300, 320), (352, 352), (384, 384)):
         el = B * H * N * dp
         assert L.fa_fwd_general_workspace_size(B, H, N, d) == 3 * a256(2 * el) + a256(4 * el)
         assert L.fa_bwd_general_workspace_size(B, H, N, d, 1) == 4 * a256(2 * el) + 4 * a256(4 * el) + a256(4 * B * H * N)
     assert L.fa_fwd_general_workspace_size(B, H, N, 0) == 0
-    assert L.fa_fwd_general_workspace_size(B, H, N, 257) == 0
+    assert L.fa_fwd_general_workspace_size(B, H, N, 385) == 0
     assert L.fa_bwd_general_workspace_size(B, H, N, 96, 5) == 0
 
     # d = 100 is not a multiple of 8, so these calls take the padded-copy path, the one that
@@ -234,7 +235,7 @@ def test_general_entries_validate_before_launching(L):
                                 ctypes.c_void_p(ws), wsb, None)
 
     assert gfwd(d=0) == FA_ERR_UNSUPPORTED
-    assert gfwd(d=257) == FA_ERR_UNSUPPORTED
+    assert gfwd(d=385) == FA_ERR_UNSUPPORTED
     assert gfwd(q=0) == FA_ERR_INVALID_ARG
     assert gfwd(q=P + 1) == FA_ERR_INVALID_ARG                 # bf16 view on an odd byte address
     assert gfwd(lse=P + 256 * MB + 4) == FA_ERR_INVALID_ARG    # lse must be 16-byte aligned
@@ -297,6 +298,7 @@ def test_dropout_entries_validate_and_keep_scale(L):
     assert dfwd(p=1.0) == FA_ERR_INVALID_ARG
     assert dfwd(p=float("nan")) == FA_ERR_INVALID_ARG
     assert dfwd(d=100) == FA_ERR_UNSUPPORTED
+    assert dfwd(d=320) == FA_ERR_UNSUPPORTED           # no dropout kernels above 256
     assert dfwd(q=0) == FA_ERR_INVALID_ARG
     assert dfwd(o=P + 8) == FA_ERR_INVALID_ARG         # o overlaps q
     need = L.fa_bwd_workspace_size(B, H, N, d, 1)
@@ -326,7 +328,7 @@ def test_dropout_entries_validate_and_keep_scale(L):
                                         ctypes.c_void_p(P + 512 * MB), wsb, None)
 
     assert gfwd(p=1.0) == FA_ERR_INVALID_ARG
-    assert gfwd(d=300) == FA_ERR_UNSUPPORTED
+    assert gfwd(d=300) == FA_ERR_UNSUPPORTED           # no dropout kernels above 256
     assert gfwd(wsb=gneed - 1) == FA_ERR_WORKSPACE
     bneed = L.fa_bwd_general_workspace_size(B, H, N, dg, 1)
 

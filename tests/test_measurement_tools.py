@@ -16,6 +16,12 @@ from exact_attention_102_amd.traffic import classify
     ("void fa::dkdv_wide_kernel<128, 128, 64, 4, true, false>(fa::BwdArgs)", ("dkdv", "causal")),
     ("void fa::dkdv_wide_kernel<128, 96, 32, 4, true, true>(fa::BwdArgs)", ("dkdv_atomic", "causal")),
     ("void fa::preprocess_kernel<128>(fa::PreArgs)", ("preprocess", None)),
+    # forward with optimistic statistics: <D, DV, tile, waves, occupancy, CAUSAL, DROP, OPT>
+    ("void fa::fwd_kernel<128, 128, 32, 4, 3, false, false, true>(fa::FwdArgs)", ("fwd", "full")),
+    ("void fa::fwd_kernel<128, 128, 32, 4, 3, true, false, true>(fa::FwdArgs)", ("fwd", "causal")),
+    # column-window dK/dV above 256: <D, DV, window, BQ, waves, CAUSAL, ATOMIC>
+    ("void fa::dkdv_split_kernel<384, 320, 128, 32, 4, true, true>(fa::BwdArgs)", ("dkdv_atomic", "causal")),
+    ("void fa::dkdv_split_kernel<384, 384, 128, 32, 4, false, false>(fa::BwdArgs)", ("dkdv", "full")),
 ])
 def test_classify(name, expected):
     assert classify(name) == expected
@@ -24,6 +30,7 @@ def test_classify(name, expected):
 @pytest.mark.parametrize("name", [
     # dropout kernels (last template argument true) are timed by their own report
     "void fa::fwd_kernel<128, 128, 64, 4, 2, false, true>(fa::FwdArgs)",
+    "void fa::fwd_kernel<128, 128, 64, 4, 2, false, true, false>(fa::FwdArgs)",
     "void fa::dkdv_kernel<128, 128, 64, 4, false, false, 0, false, true>(fa::BwdArgs)",
     "void elementwise_copy_kernel(float*)",
 ])

@@ -19,9 +19,12 @@ from parity_util import (VARIANTS, check_backward, check_forward, gpu_backward, 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
 
 SMALL = [(1, 2, 1), (1, 1, 33), (1, 2, 77), (2, 2, 300), (1, 2, 512)]
+# head dims with kernels of their own: up to 256 on 64/128/256-wide tiles, 288..384 on
+# 384-wide tiles (the dK/dV pass in 128-column windows)
+DS = [64, 96, 128, 192, 256, 288, 320, 352, 384]
 
 
-@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("d", DS)
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("bhn", SMALL, ids=lambda t: "B%dH%dN%d" % t)
 def test_small_fwd_bwd(d, causal, bhn):
@@ -43,7 +46,7 @@ def _all_cfgs(pass_id, d):
     return list(range(fa_num_configs(pass_id, d)))
 
 
-@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("d", DS)
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_tile_config(d, causal):
     from exact_attention_102_amd import PASS_DKDV, PASS_DKDV_ATOMIC, PASS_DQ, PASS_FWD
@@ -100,7 +103,7 @@ def test_sharp_softmax_small():
             check_backward(gpu_backward(dev, o, lse, causal, scale, var), refs)
 
 
-@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("d", DS)
 def test_causal_row_zero_is_v0(d):
     B, H, N = 2, 2, 200
     scale = 1.0 / math.sqrt(d)
@@ -116,7 +119,7 @@ def test_causal_row_zero_is_v0(d):
     assert np.max(np.abs(lse[:, :, 0].cpu().numpy() - want)) <= 1e-5
 
 
-@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("d", DS)
 def test_7gemm_is_bitwise_deterministic(d):
     B, H, N = 2, 2, 333
     scale = 1.0 / math.sqrt(d)
@@ -150,6 +153,8 @@ WORKLOAD_CASES = [
     ("b4_h16_n2048_d128_causal", [0, 37]),
     ("b2_h16_n8192_d128_causal", [5]),
     ("b4_h8_n4096_d256", [31]),
+    ("b2_h8_n4096_d384", [0, 15]),
+    ("b2_h8_n4096_d384_causal", [9]),
     ("b1_h32_n16384_d64_causal_sharp", [17]),
 ]
 

@@ -48,6 +48,8 @@ WORKLOADS = {
     "b2_h16_n8192_d128_causal": Workload("b2_h16_n8192_d128_causal", 2, 16, 8192, 128, True, 3),
     "b2_h16_n8192_d128_full": Workload("b2_h16_n8192_d128_full", 2, 16, 8192, 128, False, 3),
     "b4_h8_n4096_d256": Workload("b4_h8_n4096_d256", 4, 8, 4096, 256, False, 4),
+    "b2_h8_n4096_d384": Workload("b2_h8_n4096_d384", 2, 8, 4096, 384, False, 6),
+    "b2_h8_n4096_d384_causal": Workload("b2_h8_n4096_d384_causal", 2, 8, 4096, 384, True, 6),
     "b1_h32_n16384_d64_causal_sharp": Workload("b1_h32_n16384_d64_causal_sharp", 1, 32, 16384, 64, True, 5,
                                                 qk_mult=8.0),
 }
