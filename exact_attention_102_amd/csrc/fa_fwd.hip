@@ -50,6 +50,12 @@ struct FwdTileMath {
   static constexpr int KK = DV / 16;  // k-steps of Q K^T
   static constexpr int kAhead = 3;
   static constexpr int kAheadV = 3;
+  // O accumulators in accumulation registers: the one-wave-per-SIMD shapes (d >= 192).
+  // Under the causal mask these waves also run the tiles past their diagonal (fully
+  // masked: P = 0, O unchanged) instead of branching around them: at the join of a
+  // skipped and a computed tile the compiler copies all of O out of and back into the
+  // accumulation registers every tile.
+  static constexpr bool kAgprO = DV >= 192;
 
   // One K/V tile for one wave: 32 queries (one per lane column) x BC keys.
   __device__ __forceinline__ static void step(const LDS char* kt, const LDS char* vt, const bf16x8 (&qf)[KK],
@@ -133,10 +139,28 @@ struct FwdTileMath {
         m_run = m_new;
         l_run *= alpha;
         lb_run *= alpha;
+        if constexpr (kAgprO) {
+          // O lives in accumulation registers (one wave per SIMD): scale it in place.  With
+          // plain multiplies the compiler copies all of O into vector registers at the top of
+          // every tile, whether or not the tile rescales.
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
+          for (int db = 0; db < DB; ++db) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+            for (int r = 0; r < 16; ++r) {
+              float x = o[db][r], t;
+              asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                           : "+a"(x), "=&v"(t)
+                           : "v"(alpha));
+              o[db][r] = x;
+            }
+          }
+          asm volatile("s_nop 2");  // accumulation-register writes before the next MFMA reads them
+        } else {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          }
         }
       }
       const float nm = -m_run;
@@ -256,7 +280,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       kdma.issue(Kh, (j + 1) * BC, N, kbuf1, wave, lane);
       vdma.issue(Vh, (j + 1) * BC, N, vbuf1, wave, lane);
     }
-    if (!CAUSAL || j * BC <= q_w + 31)
+    if (!CAUSAL || M::kAgprO || j * BC <= q_w + 31)
       M::step(kbuf0, vbuf0, qf, o, m_run, l_run, lb_run, j * BC, q_w, qi, N, c, fk, fv, g, dc, j == 0);
     wait_tile();
     __syncthreads();
@@ -269,7 +293,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
       kdma.issue(Kh, (j + 2) * BC, N, kbuf0, wave, lane);
       vdma.issue(Vh, (j + 2) * BC, N, vbuf0, wave, lane);
     }
-    if (!CAUSAL || (j + 1) * BC <= q_w + 31)
+    if (!CAUSAL || M::kAgprO || (j + 1) * BC <= q_w + 31)
       M::step(kbuf1, vbuf1, qf, o, m_run, l_run, lb_run, (j + 1) * BC, q_w, qi, N, c, fk, fv, g, dc, false);
     wait_tile();
     __syncthreads();
