@@ -664,26 +664,32 @@ struct DkdvWideMath {
         // S of both key blocks first (Q fragments shared), then P; then dP (dO fragments
         // shared) and dS.  Only one of S and dP is live at a time, which keeps both out
         // of the accumulation registers the dK/dV accumulators fill.
+        // S and dP land in vector registers (mfma32v_*): the elementwise work reads them
+        // there, and the dK/dV accumulators keep the accumulation registers to themselves.
+        // The fragment reads run two k-steps ahead through three rotating slots.
         f32x16 p[2];
+        {
+          bf16x8 qa[3], k0f[3], k1f[3];
+          auto ld = [&](int kk) {
+            qa[kk % 3] = fr.row(qtl, qb * 32, kk);
+            k0f[kk % 3] = pk.row(ktile, wave * 64, kk);
+            k1f[kk % 3] = pk.row(ktile, wave * 64 + 32, kk);
+          };
+          ld(0);
+          ld(1);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) p[b] = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 qa = fr.row(qtl, qb * 32, kk);
-          const bf16x8 k0f = pk.row(ktile, wave * 64, kk);
-          const bf16x8 k1f = pk.row(ktile, wave * 64 + 32, kk);
-          p[0] = mfma32(qa, k0f, p[0]);
-          p[1] = mfma32(qa, k1f, p[1]);
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) ld(kk + 2);
+            const int sl = kk % 3;
+            if (kk == 0)
+              mfma32v_first2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
+            else if (kk == KK - 1)
+              mfma32v_last2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
+            else
+              mfma32v_step2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        // fragment reads (three per k-step) run two k-steps ahead of their MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK - 2; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_barrier(0);
         // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
         float l2[16];
 #pragma unroll
@@ -718,23 +724,23 @@ struct DkdvWideMath {
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x16 dp[2];
+        {
+          bf16x8 da[3];
+          da[0] = fr.row(dotl, qb * 32, 0);
+          da[1] = fr.row(dotl, qb * 32, 1);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) dp[b] = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 da = fr.row(dotl, qb * 32, kk);
-          dp[0] = mfma32(da, vf[0][kk], dp[0]);
-          dp[1] = mfma32(da, vf[1][kk], dp[1]);
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) da[(kk + 2) % 3] = fr.row(dotl, qb * 32, kk + 2);
+            const int sl = kk % 3;
+            if (kk == 0)
+              mfma32v_first2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
+            else if (kk == KK - 1)
+              mfma32v_last2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
+            else
+              mfma32v_step2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        // dO fragment reads run two k-steps ahead
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int kk = 0; kk < KK - 2; ++kk) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-        __builtin_amdgcn_sched_barrier(0);
         float dl[16];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {

@@ -33,6 +33,39 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The same MFMA written so that its result lands in vector registers, for short-lived
+// products that VALU work consumes (S and dP in the dK/dV kernels) in kernels whose
+// long-lived accumulators fill the accumulation registers: there the compiler gives
+// every MFMA the accumulation-register form, and each such result is then read back one
+// register at a time.  The compiler does not see these statements as MFMAs, so a chain
+// starts with C = 0 as an inline constant (no VALU-written register feeds it) and ends
+// with the result wait inside the same statement (s_nop 7 + s_nop 3 + the second MFMA:
+// at least 12 wait states before any instruction after the statement can read a result).
+// Dependent MFMAs of a chain (C = the previous D, same registers) issue back to back.
+// Each statement runs one k-step of two products that share the A operand.
+__device__ __forceinline__ void mfma32v_first2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, 0"
+      : "=&v"(d0), "=&v"(d1)
+      : "v"(a), "v"(b0), "v"(b1));
+}
+__device__ __forceinline__ void mfma32v_step2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+      : "+v"(d0), "+v"(d1)
+      : "v"(a), "v"(b0), "v"(b1));
+}
+__device__ __forceinline__ void mfma32v_last2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+  asm volatile(
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1\n\t"
+      "s_nop 7\n\t"
+      "s_nop 3"
+      : "+v"(d0), "+v"(d1)
+      : "v"(a), "v"(b0), "v"(b1));
+}
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
