@@ -150,6 +150,9 @@ struct DkdvMath {
   // of registers.
   static constexpr bool kPipe =
       !DROP && QBN >= 2 && D == 64 && DV == 64 && (ATOMIC ? NW == 4 : NW == 8);
+  // S and dP as vector-register MFMAs (mfma32v_*) where the dK/dV accumulators live in
+  // the accumulation registers: workgroups of at most 4 waves (one wave per SIMD)
+  static constexpr bool kVgprSP = NW <= 4;
 
   __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
@@ -294,35 +297,66 @@ struct DkdvMath {
           for (int h = 0; h < 2; ++h)
             dr[h] = transpose8_b16(drop_draws(dc, (kw >> 3) + (l32 >> 3), qbase + 16 * h + 8 * g + (l32 & 7)), lane);
         }
-        f32x16 s = zero16(), dp = zero16();
+        f32x16 s, dp;
+        if constexpr (kVgprSP) {
+          // S and dP in vector registers (see the wide kernel); fragment reads two k-steps
+          // ahead through three rotating slots
+          bf16x8 qa[3], da[3], kb[3], vb[3];
+          auto ld = [&](int kk) {
+            qa[kk % 3] = fr.row(qtl, qb * 32, kk);
+            da[kk % 3] = fr.row(dotl, qb * 32, kk);
+            if constexpr (K_LDS) {
+              kb[kk % 3] = pk.row(ktile, wave * 32, kk);
+            } else {
+              kb[kk % 3] = kf[kk];
+            }
+            if constexpr (V_LDS) {
+              vb[kk % 3] = pv.row(vtile, wave * 32, kk);
+            } else {
+              vb[kk % 3] = vf[kk];
+            }
+          };
+          ld(0);
+          ld(1);
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          bf16x8 kb, vb;
-          if constexpr (K_LDS) {
-            kb = pk.row(ktile, wave * 32, kk);
-          } else {
-            kb = kf[kk];
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) ld(kk + 2);
+            const int sl = kk % 3;
+            mfma32v_kstep(kk, KK, s, dp, qa[sl], kb[sl], da[sl], vb[sl]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if constexpr (V_LDS) {
-            vb = pv.row(vtile, wave * 32, kk);
-          } else {
-            vb = vf[kk];
-          }
-          s = mfma32(fr.row(qtl, qb * 32, kk), kb, s);
-          dp = mfma32(fr.row(dotl, qb * 32, kk), vb, dp);
-          if constexpr (!kReadAhead) fence_every<4>(kk);
-        }
-        // Interleave: fragment reads run two k-steps ahead of their MFMAs, so LDS
-        // latency hides under the previous products instead of stalling the wave.
-        if constexpr (kReadAhead) {
-          constexpr int RPS = 2 + K_LDS + V_LDS;  // row-fragment reads per k-step
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
+        } else {
+          s = zero16();
+          dp = zero16();
 #pragma unroll
-          for (int kk = 0; kk < KK - 2; ++kk) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+          for (int kk = 0; kk < KK; ++kk) {
+            bf16x8 kb, vb;
+            if constexpr (K_LDS) {
+              kb = pk.row(ktile, wave * 32, kk);
+            } else {
+              kb = kf[kk];
+            }
+            if constexpr (V_LDS) {
+              vb = pv.row(vtile, wave * 32, kk);
+            } else {
+              vb = vf[kk];
+            }
+            s = mfma32(fr.row(qtl, qb * 32, kk), kb, s);
+            dp = mfma32(fr.row(dotl, qb * 32, kk), vb, dp);
+            if constexpr (!kReadAhead) fence_every<4>(kk);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          // Interleave: fragment reads run two k-steps ahead of their MFMAs, so LDS
+          // latency hides under the previous products instead of stalling the wave.
+          if constexpr (kReadAhead) {
+            constexpr int RPS = 2 + K_LDS + V_LDS;  // row-fragment reads per k-step
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * RPS, 0);
+#pragma unroll
+            for (int kk = 0; kk < KK - 2; ++kk) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, RPS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         // register 8h + e <-> query row qb*32 + 16h + 8g + e of the tile
@@ -681,12 +715,7 @@ struct DkdvWideMath {
           for (int kk = 0; kk < KK; ++kk) {
             if (kk + 2 < KK) ld(kk + 2);
             const int sl = kk % 3;
-            if (kk == 0)
-              mfma32v_first2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
-            else if (kk == KK - 1)
-              mfma32v_last2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
-            else
-              mfma32v_step2(p[0], p[1], qa[sl], k0f[sl], k1f[sl]);
+            mfma32v_kstep(kk, KK, p[0], p[1], qa[sl], k0f[sl], qa[sl], k1f[sl]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -732,12 +761,7 @@ struct DkdvWideMath {
           for (int kk = 0; kk < KK; ++kk) {
             if (kk + 2 < KK) da[(kk + 2) % 3] = fr.row(dotl, qb * 32, kk + 2);
             const int sl = kk % 3;
-            if (kk == 0)
-              mfma32v_first2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
-            else if (kk == KK - 1)
-              mfma32v_last2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
-            else
-              mfma32v_step2(dp[0], dp[1], da[sl], vf[0][kk], vf[1][kk]);
+            mfma32v_kstep(kk, KK, dp[0], dp[1], da[sl], vf[0][kk], da[sl], vf[1][kk]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -1056,7 +1080,8 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
 //   dQ^T += K^T dS^T                 A = transposed reads of the K tile
 // No atomics: each dq element is written once, so results are reproducible bit
 // for bit (issue 1172: the 7-GEMM form is deterministic).
-template <int D, int DV, int BC, bool CAUSAL, bool DROP>
+// VSP: S and dP as vector-register MFMAs (mfma32v_*), for the one-wave-per-SIMD shapes.
+template <int D, int DV, int BC, bool CAUSAL, bool DROP, bool VSP = false>
 struct DqMath {
   static constexpr int KB = BC / 32;
   static constexpr int DB = DV / 32;
@@ -1077,12 +1102,32 @@ struct DqMath {
     bf16x8 dsb[2 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s, dp;
+      if constexpr (VSP) {
+        // S and dP in vector registers (the dQ accumulators hold the accumulation
+        // registers at one wave per SIMD); K and V fragment reads two k-steps ahead
+        bf16x8 ka[3], va[3];
+        auto ld = [&](int kk) {
+          ka[kk % 3] = fkr.row(kt, kb * 32, kk);
+          va[kk % 3] = fvr.row(vt, kb * 32, kk);
+        };
+        ld(0);
+        ld(1);
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        s = mfma32(fkr.row(kt, kb * 32, kk), qf[kk], s);
-        dp = mfma32(fvr.row(vt, kb * 32, kk), dof[kk], dp);
-        fence_every<4>(kk);
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 2 < KK) ld(kk + 2);
+          mfma32v_kstep(kk, KK, s, dp, ka[kk % 3], qf[kk], va[kk % 3], dof[kk]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        s = zero16();
+        dp = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          s = mfma32(fkr.row(kt, kb * 32, kk), qf[kk], s);
+          dp = mfma32(fvr.row(vt, kb * 32, kk), dof[kk], dp);
+          fence_every<4>(kk);
+        }
       }
       // keys past the end, and (causal) keys after the query, score -inf (P = 0).  A
       // pass of its own, taken only on tiles that need it; the empty asm statement
@@ -1116,7 +1161,7 @@ struct DqMath {
 
 template <int D, int DV, int BC, int NW, int OCC, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
-  using M = DqMath<D, DV, BC, CAUSAL, DROP>;
+  using M = DqMath<D, DV, BC, CAUSAL, DROP, OCC == 1 && DV <= 352>;
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;
   constexpr int DB = M::DB, KK = M::KK;
@@ -1352,12 +1397,32 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_split_kernel(BwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       bf16x8 sb0, sb1;
       if (qbase < N && (!CAUSAL || qbase + 31 >= kw)) {
-        f32x16 sc = zero16(), dp = zero16();
+        // S and dP in vector registers (mfma32v_*; up to DV = 320, above that the extra
+        // vector registers spill); Q and dO fragment reads two k-steps ahead
+        f32x16 sc, dp;
+        if constexpr (DV > 320) {
+          sc = zero16();
+          dp = zero16();
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          sc = mfma32(fr.row(qtl, qb * 32, kk), kf[kk], sc);
-          dp = mfma32(fr.row(dotl, qb * 32, kk), vf[kk], dp);
-          fence_every<4>(kk);
+          for (int kk = 0; kk < KK; ++kk) {
+            sc = mfma32(fr.row(qtl, qb * 32, kk), kf[kk], sc);
+            dp = mfma32(fr.row(dotl, qb * 32, kk), vf[kk], dp);
+            fence_every<4>(kk);
+          }
+        } else {
+          bf16x8 qa[3], da[3];
+          auto ld = [&](int kk) {
+            qa[kk % 3] = fr.row(qtl, qb * 32, kk);
+            da[kk % 3] = fr.row(dotl, qb * 32, kk);
+          };
+          ld(0);
+          ld(1);
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) ld(kk + 2);
+            mfma32v_kstep(kk, KK, sc, dp, qa[kk % 3], kf[kk], da[kk % 3], vf[kk]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         float l2[16], dl[16];

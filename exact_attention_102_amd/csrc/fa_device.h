@@ -37,35 +37,65 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // products that VALU work consumes (S and dP in the dK/dV kernels) in kernels whose
 // long-lived accumulators fill the accumulation registers: there the compiler gives
 // every MFMA the accumulation-register form, and each such result is then read back one
-// register at a time.  The compiler does not see these statements as MFMAs, so a chain
-// starts with C = 0 as an inline constant (no VALU-written register feeds it) and ends
-// with the result wait inside the same statement (s_nop 7 + s_nop 3 + the second MFMA:
-// at least 12 wait states before any instruction after the statement can read a result).
+// register at a time.  The compiler does not see these statements as MFMAs, so each
+// statement opens with s_nop 1: an MFMA must not read a register in the 2 wait states
+// after a VALU instruction wrote it, and under register pressure the compiler refills
+// operand registers with VALU moves (v_accvgpr_read of a value it parked in an
+// accumulation register) right before the statement.  A chain starts with C = 0 as an
+// inline constant and ends with the result wait inside the same statement (at least 12 wait states before any
+// instruction after the statement can read a result: s_nop 7 + s_nop 3 after the second
+// MFMA of a pair, s_nop 7 + s_nop 4 after a single one).
 // Dependent MFMAs of a chain (C = the previous D, same registers) issue back to back.
-// Each statement runs one k-step of two products that share the A operand.
-__device__ __forceinline__ void mfma32v_first2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+// Each statement runs one k-step of two products, d0 += a0 b0 and d1 += a1 b1.
+__device__ __forceinline__ void mfma32v_first(f32x16& d0, f32x16& d1, bf16x8 a0, bf16x8 b0, bf16x8 a1,
+                                              bf16x8 b1) {
   asm volatile(
+      "s_nop 1\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %3, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, 0"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, 0"
       : "=&v"(d0), "=&v"(d1)
-      : "v"(a), "v"(b0), "v"(b1));
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
-__device__ __forceinline__ void mfma32v_step2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+__device__ __forceinline__ void mfma32v_step(f32x16& d0, f32x16& d1, bf16x8 a0, bf16x8 b0, bf16x8 a1,
+                                             bf16x8 b1) {
   asm volatile(
+      "s_nop 1\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1"
       : "+v"(d0), "+v"(d1)
-      : "v"(a), "v"(b0), "v"(b1));
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
-__device__ __forceinline__ void mfma32v_last2(f32x16& d0, f32x16& d1, bf16x8 a, bf16x8 b0, bf16x8 b1) {
+__device__ __forceinline__ void mfma32v_last(f32x16& d0, f32x16& d1, bf16x8 a0, bf16x8 b0, bf16x8 a1,
+                                             bf16x8 b1) {
   asm volatile(
+      "s_nop 1\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %5, %1\n\t"
       "s_nop 7\n\t"
       "s_nop 3"
       : "+v"(d0), "+v"(d1)
-      : "v"(a), "v"(b0), "v"(b1));
+      : "v"(a0), "v"(b0), "v"(a1), "v"(b1));
 }
+// k-step kk of KK of the pair (the first step starts from 0, the last ends with the wait)
+__device__ __forceinline__ void mfma32v_kstep(int kk, int KK, f32x16& d0, f32x16& d1, bf16x8 a0, bf16x8 b0,
+                                              bf16x8 a1, bf16x8 b1) {
+  if (kk == 0)
+    mfma32v_first(d0, d1, a0, b0, a1, b1);
+  else if (kk == KK - 1)
+    mfma32v_last(d0, d1, a0, b0, a1, b1);
+  else
+    mfma32v_step(d0, d1, a0, b0, a1, b1);
+}
+// One product alone (d += a b), same conventions.
+__device__ __forceinline__ void mfma32v_kstep1(int kk, int KK, f32x16& d, bf16x8 a, bf16x8 b) {
+  if (kk == 0)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  else if (kk == KK - 1)
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 4" : "+v"(d) : "v"(a), "v"(b));
+  else
+    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

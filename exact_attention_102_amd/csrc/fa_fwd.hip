@@ -70,22 +70,43 @@ struct FwdTileMath {
       for (int ks = 0; ks < 2 * KB; ++ks) dr[ks] = drop_draws(dc, ((k0 + 8 * g) >> 3) + 2 * ks, qi);
     }
     f32x16 s[KB];
+    if constexpr (kAgprO && KB <= 2) {
+      // S in vector registers (mfma32v_*; O holds the accumulation registers); K
+      // fragment reads two k-steps ahead through three rotating slots
+      bf16x8 ka[3][KB];
+      auto ld = [&](int kk) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
+        for (int kb = 0; kb < KB; ++kb) ka[kk % 3][kb] = fk.row(kt, kb * 32, kk);
+      };
+      ld(0);
+      ld(1);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 2 < KK) ld(kk + 2);
+        if constexpr (KB == 2)
+          mfma32v_kstep(kk, KK, s[0], s[1], ka[kk % 3][0], qf[kk], ka[kk % 3][1], qf[kk]);
+        else
+          mfma32v_kstep1(kk, KK, s[0], ka[kk % 3][0], qf[kk]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(fk.row(kt, kb * 32, kk), qf[kk], s[kb]);
+      for (int kb = 0; kb < KB; ++kb) s[kb] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) s[kb] = mfma32(fk.row(kt, kb * 32, kk), qf[kk], s[kb]);
+      }
+      // K fragment reads run kAhead k-steps ahead of their MFMAs (LDS latency hides
+      // under the previous k-steps' products)
+      __builtin_amdgcn_sched_group_barrier(0x100, KB * kAhead, 0);
+#pragma unroll
+      for (int kk = 0; kk < KK - kAhead; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KB * kAhead, 0);
     }
-    // K fragment reads run kAhead k-steps ahead of their MFMAs (LDS latency hides
-    // under the previous k-steps' products)
-    __builtin_amdgcn_sched_group_barrier(0x100, KB * kAhead, 0);
-#pragma unroll
-    for (int kk = 0; kk < KK - kAhead; ++kk) {
-      __builtin_amdgcn_sched_group_barrier(0x008, KB, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, KB * kAhead, 0);
     // keys past the end, and (causal) keys after the query, score -inf
     if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > q_w)) {
 #pragma unroll

@@ -11,7 +11,13 @@ that distance is 12: the smallest the compiler inserts anywhere in these kernels
 inside one basic block.  This tool compiles the kernels' device assembly, builds
 each function's control-flow graph and, for every MFMA, walks every path forward
 to each instruction that reads one of its result registers before they are
-overwritten, reporting paths shorter than the required distance.  A compiler that
+overwritten, reporting paths shorter than the required distance.  It also checks the
+other direction: an MFMA may not read (as A, B or C) a register that a VALU instruction
+wrote in the 2 wait states before it.  The compiler keeps both distances for the MFMAs it
+emits; MFMAs written as inline assembly (vector-register results) are invisible to it,
+and under register pressure it refilled their operand registers with v_accvgpr_read one
+wait state before such a statement (a wrong dQ at d = 288 until every statement opened
+with s_nop 1).  A compiler that
 places the reads after a join whose other predecessor branches straight from the
 MFMA's block can leave such a path; that is how a variant of the atomic dK/dV
 kernel (its dS^T zeroing moved into a wave-uniform branch) read dK accumulators one
@@ -38,6 +44,8 @@ KERNEL_SOURCES = ["fa_fwd.hip", "fa_bwd.hip"]
 
 # wait states between an MFMA writing its result and a VALU-side read of it, per opcode prefix
 REQUIRED = {"v_mfma_f32_32x32x16": 12}
+# wait states between a VALU instruction writing a register and an MFMA reading it (A, B or C)
+VALU_TO_MFMA = 2
 STORE_OPS = ("ds_write", "buffer_store", "global_store", "buffer_atomic", "global_atomic")
 
 
@@ -94,45 +102,66 @@ def cfg(body: str):
     return out
 
 
+def _walk(g, b, i, x, live, need, is_hit, found):
+    """Follows every control-flow path from instruction i + 1 of block b until `need` wait
+    states have passed or the registers `live` are all overwritten, recording each
+    instruction for which is_hit(op, operands, live) holds."""
+    stack = [(b, i + 1, 0, frozenset(live))]
+    seen = {}
+    while stack:
+        bb, j, w, live = stack.pop()
+        if w >= need or not live:
+            continue
+        L, succ = g[bb]
+        if j >= len(L):
+            for s in succ:
+                if seen.get((s, live), 1 << 30) > w:
+                    seen[(s, live)] = w
+                    stack.append((s, 0, w, live))
+            continue
+        y = L[j]
+        op2, t2 = split(y)
+        dst = regs(t2[0]) if t2 else set()
+        if op2.startswith(STORE_OPS):
+            dst = set()
+        if is_hit(op2, t2, live):
+            found.append((w, x, y, bb))
+        stack.append((bb, j + 1, w + wait_states(y), frozenset(live - dst)))
+
+
+def _reads_mfma_result(op, t, live):
+    if op.startswith("v_mfma"):  # A or B operand (C = the same registers is a legal chain)
+        return bool((regs(t[1]) | regs(t[2])) & live) if len(t) > 2 else False
+    src = set()
+    for tok in t[1:]:
+        src |= regs(tok)
+    if op.startswith(STORE_OPS) and t:
+        src |= regs(t[0])
+    return bool(src & live) and not op.startswith("v_readfirstlane")
+
+
+def _mfma_reads(op, t, live):
+    if not op.startswith("v_mfma") or len(t) < 4:
+        return False
+    return bool((regs(t[1]) | regs(t[2]) | regs(t[3])) & live)
+
+
 def scan_function(body: str):
-    """[(wait states, mfma, reader, reader block)] for every read closer than required."""
+    """[(wait states, writer, reader, reader block)] for every read closer than required:
+    an MFMA's result read by a VALU instruction, a store or another MFMA's A/B operand,
+    and a VALU-written register read by an MFMA."""
     g = cfg(body)
     found = []
     for b, (ins, _) in g.items():
         for i, x in enumerate(ins):
             op, toks = split(x)
-            need = next((n for p, n in REQUIRED.items() if op.startswith(p)), None)
-            if need is None:
+            if not toks:
                 continue
-            stack = [(b, i + 1, 0, frozenset(regs(toks[0])))]
-            seen = {}
-            while stack:
-                bb, j, w, live = stack.pop()
-                if w >= need or not live:
-                    continue
-                L, succ = g[bb]
-                if j >= len(L):
-                    for s in succ:
-                        if seen.get((s, live), 1 << 30) > w:
-                            seen[(s, live)] = w
-                            stack.append((s, 0, w, live))
-                    continue
-                y = L[j]
-                op2, t2 = split(y)
-                dst = regs(t2[0]) if t2 else set()
-                src = set()
-                for t in t2[1:]:
-                    src |= regs(t)
-                if op2.startswith(STORE_OPS):
-                    src |= dst
-                    dst = set()
-                if op2.startswith("v_mfma"):
-                    hit = bool((regs(t2[1]) | regs(t2[2])) & live) if len(t2) > 2 else False
-                else:
-                    hit = bool(src & live) and not op2.startswith("v_readfirstlane")
-                if hit:
-                    found.append((w, x, y, bb))
-                stack.append((bb, j + 1, w + wait_states(y), frozenset(live - dst)))
+            need = next((n for p, n in REQUIRED.items() if op.startswith(p)), None)
+            if need is not None:
+                _walk(g, b, i, x, regs(toks[0]), need, _reads_mfma_result, found)
+            elif op.startswith("v_") and not op.startswith(("v_mfma", "v_readfirstlane", "v_readlane")):
+                _walk(g, b, i, x, regs(toks[0]), VALU_TO_MFMA, _mfma_reads, found)
     return found
 
 
@@ -180,7 +209,7 @@ def main():
             bad += 1
             w, x, y, bb = min(f)
             print("%s %s: %d short path(s), fewest %d wait states: %s -> %s [%s]" % (src, fn, len(f), w, x, y, bb))
-    print("hazard audit: %d function(s) with a short MFMA-result path" % bad)
+    print("hazard audit: %d function(s) with a short MFMA-result or VALU-to-MFMA path" % bad)
     sys.exit(1 if bad else 0)
 
 

@@ -1,4 +1,4 @@
-"""CPU tests of the MFMA result-hazard audit (exact_attention_102_amd/hazard_audit.py):
+"""CPU tests of the MFMA hazard audit (exact_attention_102_amd/hazard_audit.py):
 the scanner on hand-written control flow, then the audit of the compiled kernels."""
 import os
 import shutil
@@ -42,9 +42,22 @@ def test_scanner_accepts_padded_paths_and_overwritten_registers():
     assert min(w for w, *_ in ha.scan_assembly(ab)["_Zk"]) == 0
 
 
+def test_scanner_finds_valu_writes_read_by_an_mfma():
+    """A VALU write of an MFMA operand register needs 2 wait states before the MFMA."""
+    close = "_Zk:\n\tv_accvgpr_read_b32 v41, a155\n" \
+            "\tv_mfma_f32_32x32x16_bf16 v[18:33], v[244:247], v[38:41], 0\n\ts_endpgm\n.Lfunc_end0:\n"
+    f = ha.scan_assembly(close)
+    assert min(w for w, *_ in f["_Zk"]) == 0
+    assert ha.scan_assembly(close.replace("\tv_mfma", "\ts_nop 1\n\tv_mfma")) == {}
+    # the C operand counts too; an unrelated register does not
+    c = close.replace("v[38:41], 0", "v[0:3], v[40:55]")
+    assert list(ha.scan_assembly(c)) == ["_Zk"]
+    assert ha.scan_assembly(close.replace("v41, a155", "v99, a155")) == {}
+
+
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc is needed to compile the kernels' assembly")
-def test_compiled_kernels_have_no_short_mfma_result_paths():
+def test_compiled_kernels_have_no_short_mfma_paths():
     res = ha.audit()
     bad = {src: sorted(funcs) for src, funcs in res.items() if funcs}
     assert not bad, bad
