@@ -93,20 +93,20 @@ int default_index(int pass, int d, int causal) {
     case 0:  // fwd (opt = optimistic statistics): d64 Br32x4 Bc64 three waves per SIMD opt (causal: Br32x8
              // Bc64 exact, which the sharp causal workload needs), d96 Br32x8 Bc64 opt (causal: Br32x4 Bc32
              // three waves per SIMD opt), d128 Br32x4 Bc64 two waves per SIMD opt (causal: Bc32 three opt),
-             // d192 Bc64 (causal: Bc32 opt), d256 Bc32 opt
+             // d192 and d256 Bc32 opt
       if (d == 128) return causal ? 5 : 6;
       if (d == 256) return 2;
       if (d == 96) return causal ? 3 : 4;
-      if (d == 192) return causal ? 3 : 1;
+      if (d == 192) return 3;
       return causal ? 2 : 6;  // d == 64
-    case 1:  // dkdv: d64 Bk32x8 Bq64 (K, V in registers); d192 and d256 Bk32x4 Bq32, K read from LDS; d96
-             // and d128 two key blocks per wave, Bk64x4 Bq64
-      return d == 64 ? 2 : d == 96 ? 3 : d == 128 ? 6 : 1;
+    case 1:  // dkdv: d64 Bk32x8 Bq64 and d96 Bk32x4 Bq64 (K, V in registers); d192 and d256 Bk32x4 Bq32,
+             // K read from LDS; d128 two key blocks per wave, Bk64x4 Bq64
+      return d == 64 ? 2 : d == 96 ? 0 : d == 128 ? 6 : 1;
     case 2:  // dkdv + atomic dq, K read from LDS, dQ one tile late: d64 Bk32x8 Bq64, causal d96 Bk32x8 Bq32,
              // d192 and d256 Bk32x4 Bq32; d128 and non-causal d96 two key blocks per wave, Bk64x4 Bq32
       return d == 64 ? 4 : d == 128 ? 4 : d == 96 ? (causal ? 1 : 2) : 1;
-    case 3:  // dq: d128 Bq32x8 Bc64 (both masks), the others Bq32x4 (d256, d192: Bc32)
-      return d == 128 ? 2 : 0;
+    case 3:  // dq: d128 Bq32x8 Bc64 and d96 Bq32x8 Bc64 (both masks), the others Bq32x4 (d256, d192: Bc32)
+      return d == 128 ? 2 : d == 96 ? 1 : 0;
     default: return -1;
   }
 }

@@ -1613,16 +1613,22 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   return 0;
 }
 
+// where K and V are read from (the KVL argument): registers, LDS tiles, or K from LDS
+#define FA_KVL_NAME_false " kv_regs"
+#define FA_KVL_NAME_true " kv_lds"
+#define FA_KVL_NAME_0 " kv_regs"
+#define FA_KVL_NAME_1 " kv_lds"
+#define FA_KVL_NAME_2 " k_lds"
 #define DKDV_CFG(D, BQ, NW, KVL) \
-  { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL, &launch_dkdv<D, D, BQ, NW, false, KVL> }
+  { D, 32 * (NW), BQ, NW, "dkdv d" #D " Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL, &launch_dkdv<D, D, BQ, NW, false, KVL> }
 #define DKDVA_CFG(D, BQ, NW, KVL)                                                                        \
   {                                                                                                        \
-    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                   \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL,                   \
         &launch_dkdv<D, D, BQ, NW, true, KVL>                                                              \
   }
 #define DKDVAD_CFG(D, BQ, NW, KVL)                                                                       \
   {                                                                                                        \
-    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " deferred",         \
+    D, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #D " Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL " deferred",         \
         &launch_dkdv<D, D, BQ, NW, true, KVL, true>                                                        \
   }
 // K read from the LDS tile of the dQ product, V in registers (KVL = 2)
@@ -1666,12 +1672,12 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
 // head dim DV on D-wide tiles (the table's key is DV)
 #define DKDV_CFGV(D, DV, BQ, NW, KVL)                                                                   \
   {                                                                                                        \
-    DV, 32 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,            \
+    DV, 32 * (NW), BQ, NW, "dkdv d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL,            \
         &launch_dkdv<D, DV, BQ, NW, false, KVL>                                                            \
   }
 #define DKDVA_CFGV(D, DV, BQ, NW, KVL)                                                                  \
   {                                                                                                        \
-    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,  \
+    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq d" #DV " (tiles " #D ") Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL,  \
         &launch_dkdv<D, DV, BQ, NW, true, KVL>                                                             \
   }
 #define DQ_CFGV(D, DV, BC, NW, OCC)                                                                     \
@@ -1681,12 +1687,12 @@ static int launch_dq(const BwdArgs& a, bool causal, hipStream_t stream) {
   }
 #define DKDV_DROP_CFG(D, DV, BQ, NW, KVL)                                                               \
   {                                                                                                        \
-    DV, 32 * (NW), BQ, NW, "dkdv+dropout d" #DV " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL,                    \
+    DV, 32 * (NW), BQ, NW, "dkdv+dropout d" #DV " Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL,                    \
         &launch_dkdv<D, DV, BQ, NW, false, KVL, false, true>                                               \
   }
 #define DKDVA_DROP_CFG(D, DV, BQ, NW, KVL, DEF)                                                         \
   {                                                                                                        \
-    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #DV " Bk32x" #NW " Bq" #BQ " kv_lds" #KVL " defer" #DEF, \
+    DV, 32 * (NW), BQ, NW, "dkdv+atomic-dq+dropout d" #DV " Bk32x" #NW " Bq" #BQ FA_KVL_NAME_##KVL " defer" #DEF, \
         &launch_dkdv<D, DV, BQ, NW, true, KVL, DEF, true>                                                  \
   }
 // head dims above 256: 384-wide tiles, three 128-column windows per key tile

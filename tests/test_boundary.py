@@ -186,7 +186,7 @@ def test_report_tile_counts_match_brute_force():
     from exact_attention_102_amd.report import tile_shape, tiles
 
     assert tile_shape("fwd d128 Br32x4 Bc64 occ2") == (128, 64)
-    assert tile_shape("dkdv+atomic-dq d64 Bk32x8 Bq64 kv_ldsfalse deferred") == (256, 64)
+    assert tile_shape("dkdv+atomic-dq d64 Bk32x8 Bq64 kv_regs deferred") == (256, 64)
 
     def walk(N, rows, cols, causal, keys_major):
         nr, nc = -(-N // rows), -(-N // cols)
