@@ -33,7 +33,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
 REL = 2e-2
 
 
-@pytest.mark.parametrize("N,d", [(131072, 128), (65536, 256), (262144, 64)], ids=lambda x: str(x))
+@pytest.mark.parametrize("N,d", [(131072, 128), (65536, 256), (262144, 64), (32768, 384)], ids=lambda x: str(x))
 @pytest.mark.parametrize("causal", [False, True])
 def test_longest_sequences(N, d, causal):
     B, H = 1, 1
