@@ -42,11 +42,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // after a VALU instruction wrote it, and under register pressure the compiler refills
 // operand registers with VALU moves (v_accvgpr_read of a value it parked in an
 // accumulation register) right before the statement.  A chain starts with C = 0 as an
-// inline constant and ends with the result wait inside the same statement (at least 12 wait states before any
-// instruction after the statement can read a result: s_nop 7 + s_nop 3 after the second
-// MFMA of a pair, s_nop 7 + s_nop 4 after a single one).
+// inline constant and ends with the result wait inside the same statement: at least 12
+// wait states before any instruction after the statement can read a result (s_nop 7 +
+// s_nop 3 after the second MFMA of a pair, s_nop 7 + s_nop 4 after a single one).
 // Dependent MFMAs of a chain (C = the previous D, same registers) issue back to back.
-// Each statement runs one k-step of two products, d0 += a0 b0 and d1 += a1 b1.
+// Each statement runs one k-step of two products, d0 += a0 b0 and d1 += a1 b1; a chain
+// has at least two k-steps (KK = head dim / 16 >= 4 here).
 __device__ __forceinline__ void mfma32v_first(f32x16& d0, f32x16& d1, bf16x8 a0, bf16x8 b0, bf16x8 a1,
                                               bf16x8 b1) {
   asm volatile(
