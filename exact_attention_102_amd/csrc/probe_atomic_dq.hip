@@ -15,6 +15,8 @@
 //                  cache-policy bits A (gfx950: 1 = sc0, 2 = nt, 16 = sc1)
 //   global scope=S global atomics at memory scope S (workgroup, agent)
 //   plain stores   the same values written into per-key-tile partial buffers
+//   rows of 64     buffer atomics, each instruction one row of 64 consecutive columns
+//                  (the kernel's instructions cover two rows of 32)
 // and two work mappings: "xcd" keeps every key tile of a head on one XCD (the
 // kernel's mapping; workgroup x runs on XCD x % 8), "spread" puts a head's key
 // tiles on different XCDs.  A variant whose adds were performed in a per-XCD L2
@@ -48,7 +50,8 @@ __device__ int xcd_item(int x, int total) {
 }
 
 // KIND: 0 buffer atomic (cache policy AUX), 1 global atomic workgroup scope,
-// 2 global atomic agent scope, 3 plain stores into per-key-tile partials.
+// 2 global atomic agent scope, 3 plain stores into per-key-tile partials, 4 buffer
+// atomics with each instruction covering one row of 64 consecutive columns.
 template <int D, int KIND, int AUX>
 __global__ __launch_bounds__(NW * 64) void dq_pattern(float* dq, int N, int nkt, int spread) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 5, l32 = lane & 31;
@@ -63,6 +66,19 @@ __global__ __launch_bounds__(NW * 64) void dq_pattern(float* dq, int N, int nkt,
       __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, (int)((unsigned)N * (unsigned)(D * 4)), 0x00020000);
   for (int it = 0; it < nqt; ++it) {
     const int q0 = it * BQ;
+    if constexpr (KIND == 4) {
+      // the same adds with one row of 64 consecutive columns per instruction: wave w
+      // takes rows w * 8 .. w * 8 + 7 of the query tile, lane l column 64 p + l
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int pcol = 0; pcol < DB / 2; ++pcol) {
+          const unsigned o = ((unsigned)(q0 + wave * 8 + i) * D + pcol * 64 + lane) * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(1.0f, rs, o, 0, AUX);
+        }
+      }
+      continue;
+    }
     for (int db = wave; db < DB; db += NW) {
       const unsigned off = ((unsigned)(q0 + 4 * g) * D + db * 32 + l32) * 4u;
 #pragma unroll
@@ -134,6 +150,7 @@ void run_all(int B, int H, int N) {
     run<D, 0, 16>("buffer aux=16 (sc1)", B, H, N, spread, dq, part, h);
     run<D, 1, 0>("global scope=workgroup", B, H, N, spread, dq, part, h);
     run<D, 2, 0>("global scope=agent", B, H, N, spread, dq, part, h);
+    run<D, 4, 0>("buffer rows of 64 columns", B, H, N, spread, dq, part, h);
   }
   run<D, 3, 0>("plain stores to partials", B, H, N, 0, dq, part, h);
   CHECK(hipFree(dq));
