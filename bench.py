@@ -198,8 +198,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=-1, help="heads per workload in the oracle sample (-1: all)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (heads shard with no "
-              "exchange; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only (attention heads would shard across GPUs with no exchange; "
+              "no multi-GPU run is provided). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch

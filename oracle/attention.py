@@ -27,8 +27,8 @@ What is computed, and where the pages say so
       dV = P^T dO,  dP = dO V^T,  dS_i = (diag(P_i) - P_i P_i^T) dP_i,
       dQ = scale * dS K,  dK = scale * dS^T Q.
 
-Readings where the pages are silent (each also listed in the design doc)
-------------------------------------------------------------------
+Readings where the pages are silent
+-----------------------------------
 * scale multiplies Q K^T before the softmax; causal means query i sees keys
   j <= i (N_q == N_k, so top-left and bottom-right alignment coincide); masked
   scores are -inf and contribute exactly 0.

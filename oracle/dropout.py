@@ -11,7 +11,7 @@ What is computed, and where the pages say so
   dropout -- and FlashAttention fuses them into the kernel.  Dropout here is the
   usual inverted dropout on the attention probabilities: each P_ij is kept with
   probability 1 - p and scaled by the reciprocal of that probability, otherwise zeroed.
-* The pages give no random-number specification.  Reading (also in the design doc):
+* The pages give no random-number specification.  Reading:
   the keep decision for score element (b, h, i, j) comes from the counter-based
   generator Philox4x32-10 of Salmon, Moraes, Dror and Shaw, "Parallel Random
   Numbers: As Easy as 1, 2, 3" (SC '11), so any kernel can recompute any
