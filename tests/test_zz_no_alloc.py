@@ -4,7 +4,7 @@ fa_bwd_noalloc runs the same kernels as fa_bwd with the library's fixed device s
 place of the caller's workspace, so on the same inputs its results must equal fa_bwd's:
 bit for bit for everything computed without atomics (the 7-GEMM design's dQ, dK, dV and
 the 5-GEMM design's dK, dV), and to the fp32 reordering of the atomic sum for the 5-GEMM
-dQ.  Two calls in a row, the second smaller, check that the shared scratch carries
+dQ.  Calls in a row, each smaller than the one before, check that the shared scratch carries
 nothing over from the previous call.  The results are also held to the oracle's bar.
 """
 import math
@@ -17,7 +17,8 @@ from parity_util import VARIANTS, check_backward, gpu_forward, make_inputs, note
 
 pytestmark = [pytest.mark.gpu, pytest.mark.usefixtures("require_gpu")]
 
-CASES = [((2, 4, 1000, 128), True, 11), ((1, 2, 300, 64), False, 12)]   # second call smaller
+# each call smaller than the one before; the last runs the head-dim-384 kernels
+CASES = [((2, 4, 1000, 128), True, 11), ((1, 2, 300, 64), False, 12), ((1, 1, 200, 384), True, 13)]
 
 
 @pytest.mark.parametrize("variant", ["7gemm", "5gemm"])
