@@ -31,6 +31,11 @@ if ROOT not in sys.path:
 
 SIMDS = 1024  # 256 CUs x 4 SIMDs
 XCDS = 8      # GRBM_GUI_ACTIVE is summed over the XCDs
+# issue cost of one wave64 instruction on a SIMD, from the measured lane rates of
+# csrc/probe_rates.hip (v_fma_f32 70.7, v_exp_f32 29.8 lanes per clock per CU)
+VALU_CYCLES = 64 / (70.7 / 4)
+TRANS_CYCLES = 64 / (29.8 / 4)
+MFMA_FLOP = 32 * 32 * 16 * 2  # one v_mfma_f32_32x32x16_bf16
 
 
 def _one(dirname: str, suffix: str) -> str:
@@ -123,8 +128,9 @@ def sq_table(pmc_dir: str, workload: str) -> str:
                 per[d] = {"name": r["Kernel_Name"]}
                 order.append(d)
             per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    out = ["| kernel | MFMA busy % | MFMA GFLOP | VALU lane-ops / score elem | TRANS / elem | "
-           "LDS conflict cycles / LDS active |", "|---|---|---|---|---|---|"]
+    out = ["| kernel | MFMA busy % | VALU busy % (est.) | TRANS busy % (est.) | MFMA GFLOP | "
+           "VALU lane-ops / score elem | TRANS / elem | LDS conflict cycles / LDS active |",
+           "|---|---|---|---|---|---|---|---|"]
     for d in sorted(order):
         c = per[d]
         cl = classify(c["name"])
@@ -136,13 +142,23 @@ def sq_table(pmc_dir: str, workload: str) -> str:
         gflop = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / 1e9
         lds = c.get("SQ_LDS_IDX_ACTIVE", 0.0)
         conf = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else 0.0
+        # busy estimates: wave instructions x their measured issue cycles over the SIMD cycles
+        # (the MFMA instructions, counted among the VALU ones, are left out of the VALU figure)
+        n_valu, n_trans = c.get("SQ_INSTS_VALU", 0.0), c.get("SQ_INSTS_VALU_TRANS_F32", 0.0)
+        n_mfma = gflop * 1e9 / MFMA_FLOP
+        simd_cyc = cyc * SIMDS
+        trans_busy = 100.0 * n_trans * TRANS_CYCLES / simd_cyc if cyc else 0.0
+        valu_busy = 100.0 * (max(n_valu - n_mfma - n_trans, 0.0) * VALU_CYCLES + n_trans * TRANS_CYCLES) / simd_cyc \
+            if cyc else 0.0
         if kind == "preprocess":
-            out.append("| `%s` | %.1f | %.1f | - | - | %.3f |" % (c["name"], busy, gflop, conf))
+            out.append("| `%s` | %.1f | %.1f | %.1f | %.1f | - | - | %.3f |" % (c["name"], busy, valu_busy, trans_busy,
+                                                                             gflop, conf))
             continue
         pairs = w.B * w.H * (w.N * (w.N + 1) // 2 if mask == "causal" else w.N * w.N)
-        valu = c.get("SQ_INSTS_VALU", 0.0) * 64 / pairs
-        trans = c.get("SQ_INSTS_VALU_TRANS_F32", 0.0) * 64 / pairs
-        out.append("| `%s` | %.1f | %.1f | %.2f | %.2f | %.3f |" % (c["name"], busy, gflop, valu, trans, conf))
+        valu = n_valu * 64 / pairs
+        trans = n_trans * 64 / pairs
+        out.append("| `%s` | %.1f | %.1f | %.1f | %.1f | %.2f | %.2f | %.3f |" % (c["name"], busy, valu_busy, trans_busy,
+                                                                               gflop, valu, trans, conf))
     return "\n".join(out)
 
 

@@ -78,4 +78,14 @@ def test_profsum_sq_table(tmp_path):
     _write_csv(d / "run_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"], rows)
     row = sq_table(str(d), "b4_h16_n2048_d128").splitlines()[2]
     # busy = 400 / 1000 per SIMD; 1e9 MOPS x 512 flop; 7 and 1 lane-ops per score element; 25% conflicts
-    assert "| 40.0 | 512.0 | 7.00 | 1.00 | 0.250 |" in row
+    assert "| 512.0 | 7.00 | 1.00 | 0.250 |" in row
+    cells = [x.strip() for x in row.split("|")]
+    assert cells[2] == "40.0"
+    # VALU / TRANS busy estimates: instructions x measured issue cycles / (1000 cycles x 1024 SIMDs)
+    from exact_attention_102_amd.profsum import MFMA_FLOP, TRANS_CYCLES, VALU_CYCLES
+    n_mfma = 512e9 / MFMA_FLOP
+    n_valu, n_trans = pairs * 7 / 64, pairs / 64
+    want_trans = 100 * n_trans * TRANS_CYCLES / (1000 * 1024)
+    want_valu = 100 * ((n_valu - n_mfma - n_trans) * VALU_CYCLES + n_trans * TRANS_CYCLES) / (1000 * 1024)
+    assert abs(float(cells[3]) - want_valu) <= 0.05 + 1e-3 * want_valu
+    assert abs(float(cells[4]) - want_trans) <= 0.05 + 1e-3 * want_trans
