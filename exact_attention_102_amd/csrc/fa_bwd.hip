@@ -1046,28 +1046,18 @@ __global__ __launch_bounds__(NW * 64, 1) void dkdv_wide_kernel(BwdArgs a) {
     M::atomic_dq(((last - qt0) & 1) ? dst1 : dst0, ktile, dqh, last * BQ, N, a.scale, wave, g, l32, lane);
   }
 
+  // dK and dV through LDS as whole rows, each wave staging its blocks in its quarter of the
+  // K tile (free once every wave is past the last dQ product, which reads it)
+  if constexpr (ATOMIC) __syncthreads();
+  constexpr int kRegion = BK * D * 2 / NW;
+  LDS char* region = ktile + wave * kRegion;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    const int kb = key + 32 * b;
-    if (kb < N) {
-      float* dkr = a.dk + head_base(a.vdk, bh, a.H) + (size_t)kb * a.vdk.sn;
-      float* dvr = a.dv + head_base(a.vdv, bh, a.H) + (size_t)kb * a.vdv.sn;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int col = db * 32 + 8 * a4 + 4 * g;
-          const f32x4 kv = {dk[b][db][4 * a4] * a.scale, dk[b][db][4 * a4 + 1] * a.scale,
-                            dk[b][db][4 * a4 + 2] * a.scale, dk[b][db][4 * a4 + 3] * a.scale};
-          const f32x4 vv = {dv[b][db][4 * a4], dv[b][db][4 * a4 + 1], dv[b][db][4 * a4 + 2],
-                            dv[b][db][4 * a4 + 3]};
-          if (col < hd) {
-            *(f32x4*)(dkr + col) = kv;
-            *(f32x4*)(dvr + col) = vv;
-          }
-        }
-      }
-    }
+    const int kb0 = kw + 32 * b;
+    store_tile_rows<DB, kRegion>(dk[b], a.scale, region, a.dk + head_base(a.vdk, bh, a.H) + (size_t)kb0 * a.vdk.sn,
+                                 a.vdk.sn, N - kb0, hd, lane);
+    store_tile_rows<DB, kRegion>(dv[b], 1.f, region, a.dv + head_base(a.vdv, bh, a.H) + (size_t)kb0 * a.vdv.sn,
+                                 a.vdv.sn, N - kb0, hd, lane);
   }
 }
 
@@ -1165,14 +1155,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;
   constexpr int DB = M::DB, KK = M::KK;
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
-  LDS char* kbuf0 = (LDS char*)k0s;
-  LDS char* vbuf0 = (LDS char*)v0s;
-  LDS char* kbuf1 = (LDS char*)k1s;
-  LDS char* vbuf1 = (LDS char*)v1s;
+  // K, V double-buffered; one array where dQ is staged through it at the end
+  LDS char *kbuf0, *vbuf0, *kbuf1, *vbuf1;
+  if constexpr (OCC >= 2) {
+    __shared__ __attribute__((aligned(1024))) char tiles_s[4 * TILE];
+    kbuf0 = (LDS char*)tiles_s;
+    vbuf0 = kbuf0 + TILE;
+    kbuf1 = kbuf0 + 2 * TILE;
+    vbuf1 = kbuf0 + 3 * TILE;
+  } else {
+    __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+    __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+    __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+    __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+    kbuf0 = (LDS char*)k0s;
+    vbuf0 = (LDS char*)v0s;
+    kbuf1 = (LDS char*)k1s;
+    vbuf1 = (LDS char*)v1s;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1260,7 +1260,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  if (qi < N) {
+  if constexpr (OCC >= 2) {
+    // dQ through LDS as whole rows (the tiles are free: every wave passed the last barrier)
+    constexpr int kRegion = (4 * TILE / NW) & ~1023;
+    store_tile_rows<DB, kRegion>(dq, a.scale, kbuf0 + wave * kRegion,
+                                 a.dq + head_base(a.vdq, bh, a.H) + (size_t)q_w * a.vdq.sn, a.vdq.sn, N - q_w, hd,
+                                 lane);
+  } else if (qi < N) {
     float* dqr = a.dq + head_base(a.vdq, bh, a.H) + (size_t)qi * a.vdq.sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -370,6 +370,65 @@ __device__ __forceinline__ void fence_every(int i) {
 }
 
 // ---------------------------------------------------------------------------
+// Writes one wave's 32 x 32 DB fp32 accumulator tile to global memory as whole row
+// segments.  In the C layout lane l holds row l % 32, columns 32 db + 8 a + 4 (l / 32)
+// + 0..3 (registers 4 a .. 4 a + 3 of acc[db]), so a direct store instruction writes
+// 32 rows x 32 bytes; staged through the wave's own LDS region (REGION bytes, free of
+// any other use), each store instruction instead writes 64 / CPR complete row segments
+// of CP columns.  Chunk c of row r sits at chunk position c ^ (r & SW) in the region (no
+// bank conflicts beyond the 4 cycles a 1 KB access takes either way).  The region is
+// reused pass by pass: the wave's LDS accesses complete in issue order.  Every value is
+// multiplied by its row's factor (scale, one per lane).  row0 (wave-uniform) is the
+// first row; rows from nrows on and columns from hd on are not written: lanes are
+// masked.  The buffer range (nrows rows) does not do it alone -- a version that relied
+// on it wrote rows past nrows, so the range check does not cover the scalar offset that
+// selects a store's rows.  Offsets are 32-bit (the 32 rows span less than 2^31 bytes).
+template <int DB, int REGION>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[DB], float scale, LDS char* region, float* row0,
+                                                long long sn, int nrows, int hd, int lane) {
+  constexpr int CAP = REGION / (32 * 4);  // columns of 32 rows the region holds
+  static_assert(CAP >= 32, "the staging region must hold 32 rows of 32 columns");
+  constexpr int CP = CAP >= 128 ? 128 : CAP >= 64 ? 64 : 32;  // columns per pass
+  constexpr int CPR = CP / 4;                                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                               // rows per store instruction
+  constexpr int SW = CPR < 16 ? CPR - 1 : 15;
+  constexpr int BPP = CP / 32;  // 32-column blocks per pass
+  const int l32 = lane & 31, g = lane >> 5;
+  const unsigned pitch = (unsigned)sn * 4u;  // bytes per row
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(row0, (short)0, (int)(nrows > 0 ? (unsigned)nrows * pitch : 0u), 0x00020000);
+  const int rl = lane / CPR, c = lane % CPR;  // the lane's row within a store, its chunk
+  const unsigned voff = (unsigned)rl * pitch + (unsigned)c * 16u;
+#pragma unroll
+  for (int p = 0; p < (DB + BPP - 1) / BPP; ++p) {
+#pragma unroll
+    for (int b = 0; b < BPP; ++b) {
+      const int db = p * BPP + b;
+      if (db < DB) {
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int cw = 8 * b + 2 * a4 + g;
+          const f32x4 v = {acc[db][4 * a4] * scale, acc[db][4 * a4 + 1] * scale, acc[db][4 * a4 + 2] * scale,
+                           acc[db][4 * a4 + 3] * scale};
+          *(LDS f32x4*)(region + l32 * (CP * 4) + ((cw ^ (l32 & SW)) << 4)) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one block's values at a time (register pressure)
+      }
+    }
+    const int col = p * CP + 4 * c;
+    const bool live = col < hd && col < 32 * DB;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + rl;
+      const f32x4 v = *(const LDS f32x4*)(region + r * (CP * 4) + ((c ^ (r & SW)) << 4));
+      if (live && r < nrows)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff + (unsigned)(p * CP * 4),
+                                               (int)((unsigned)(RPI * i) * pitch), 0);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Reductions across the two 32-lane halves (lane l and lane l ^ 32), which hold
 // the two halves of a 32-key (or 32-query) block in the C layout.
 __device__ __forceinline__ float half_swap_max(float x) {

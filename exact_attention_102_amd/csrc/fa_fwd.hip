@@ -234,14 +234,24 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
   constexpr int BR = 32 * NW;
   constexpr int TILE = BC * D * 2;  // bytes of one K or V tile
   constexpr int DB = M::DB, KK = M::KK;
-  __shared__ __attribute__((aligned(1024))) char k0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v0s[TILE];
-  __shared__ __attribute__((aligned(1024))) char k1s[TILE];
-  __shared__ __attribute__((aligned(1024))) char v1s[TILE];
-  LDS char* kbuf0 = (LDS char*)k0s;
-  LDS char* vbuf0 = (LDS char*)v0s;
-  LDS char* kbuf1 = (LDS char*)k1s;
-  LDS char* vbuf1 = (LDS char*)v1s;
+  // K, V double-buffered; one array where the output is staged through it at the end
+  LDS char *kbuf0, *vbuf0, *kbuf1, *vbuf1;
+  if constexpr (OCC >= 2) {
+    __shared__ __attribute__((aligned(1024))) char tiles_s[4 * TILE];
+    kbuf0 = (LDS char*)tiles_s;
+    vbuf0 = kbuf0 + TILE;
+    kbuf1 = kbuf0 + 2 * TILE;
+    vbuf1 = kbuf0 + 3 * TILE;
+  } else {
+    __shared__ __attribute__((aligned(1024))) char k0s[TILE];
+    __shared__ __attribute__((aligned(1024))) char v0s[TILE];
+    __shared__ __attribute__((aligned(1024))) char k1s[TILE];
+    __shared__ __attribute__((aligned(1024))) char v1s[TILE];
+    kbuf0 = (LDS char*)k0s;
+    vbuf0 = (LDS char*)v0s;
+    kbuf1 = (LDS char*)k1s;
+    vbuf1 = (LDS char*)v1s;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -322,7 +332,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
 
   const float lt = half_swap_sum(l_run);
   const float inv = (DROP ? a.drop_scale : 1.f) / half_swap_sum(lb_run);
-  if (qi < N) {
+  if constexpr (OCC >= 2) {
+    // O through LDS as whole rows (the tiles are free: every wave passed the last barrier).
+    // The one-wave-per-SIMD shapes store directly: the staging's extra registers cost
+    // them more than the wider stores gain.
+    constexpr int kRegion = (4 * TILE / NW) & ~1023;
+    store_tile_rows<DB, kRegion>(o, inv, kbuf0 + wave * kRegion,
+                                 a.o + head_base(a.vo, bh, a.H) + (size_t)q_w * a.vo.sn, a.vo.sn, N - q_w, hd, lane);
+  } else if (qi < N) {
     float* orow = a.o + head_base(a.vo, bh, a.H) + (size_t)qi * a.vo.sn;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -334,8 +351,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void fwd_kernel(FwdArgs a) {
         if (col < hd) *(f32x4*)(orow + col) = val;
       }
     }
-    if (g == 0) a.lse[(size_t)bh * N + qi] = (m_run + log2f(lt)) * kLn2;
   }
+  if (qi < N && g == 0) a.lse[(size_t)bh * N + qi] = (m_run + log2f(lt)) * kLn2;
 }
 
 template <int D, int DV, int BC, int NW, int OCC, bool DROP = false, bool OPT = false>

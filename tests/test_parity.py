@@ -103,6 +103,23 @@ def test_sharp_softmax_small():
             check_backward(gpu_backward(dev, o, lse, causal, scale, var), refs)
 
 
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+@pytest.mark.parametrize("causal", [False, True])
+def test_sharp_softmax_every_fwd_config(d, causal):
+    """Peaked logits (Q, K x 8) through every forward configuration: the running maximum
+    moves often, so each configuration's rescale path (and, with optimistic statistics, its
+    fall-back to the exact maximum) runs on many tiles.  Two ragged query tiles, ragged keys."""
+    from exact_attention_102_amd import PASS_FWD
+    B, H, N = 1, 2, 333
+    scale = 1.0 / math.sqrt(d)
+    dev, host, _ = make_inputs(B, H, N, d, seed=900 + d, qk_mult=8.0)
+    ro, rl = oracle_forward(host, scale, causal)
+    for c in _all_cfgs(PASS_FWD, d):
+        note("sharp fwd cfg %d d=%d causal=%d" % (c, d, causal))
+        o, lse = gpu_forward(dev, causal, scale, cfg=c)
+        check_forward(o, lse, ro, rl)
+
+
 @pytest.mark.parametrize("d", DS)
 def test_causal_row_zero_is_v0(d):
     B, H, N = 2, 2, 200
