@@ -775,37 +775,91 @@ struct DkdvWideMath {
             for (int e = 0; e < 4; ++e) dl[8 * h + 4 * hf + e] = dd[e];
           }
         }
+        if constexpr (!ATOMIC) {
+          // dV products (they need only P), with the dS arithmetic between them (the VALU
+          // work of one wave overlaps its own MFMAs when their results go to the
+          // accumulation registers), then the dK products.  Transposed reads run one d
+          // block ahead of their MFMAs.
+          {
+            bf16x8 o[2][2];
+            o[0][0] = fc.col(dotl, qb * 32, 0);
+            o[0][1] = fc.col(dotl, qb * 32 + 16, 0);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          f32x16 ds;
+            for (int db = 0; db < DB; ++db) {
+              if (db + 1 < DB) {
+                o[(db + 1) & 1][0] = fc.col(dotl, qb * 32, db + 1);
+                o[(db + 1) & 1][1] = fc.col(dotl, qb * 32 + 16, db + 1);
+              }
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ds[r] = p[b][r] * (dp[b][r] - dl[r]);
-          sb[b][0] = pack8(ds, 0);
-          sb[b][1] = pack8(ds, 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+              for (int b = 0; b < 2; ++b) {
+                dv[b][db] = mfma32(o[db & 1][0], pb[b][0], dv[b][db]);
+                dv[b][db] = mfma32(o[db & 1][1], pb[b][1], dv[b][db]);
+              }
+              // this d block's share of the four 8-element halves of dS
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const bf16x8 o0 = fc.col(dotl, qb * 32, db);
-          const bf16x8 o1 = fc.col(dotl, qb * 32 + 16, db);
-          const bf16x8 t0 = fc.col(qtl, qb * 32, db);
-          const bf16x8 t1 = fc.col(qtl, qb * 32 + 16, db);
+              for (int hh = db * 4 / DB; hh < (db + 1) * 4 / DB; ++hh) {
+                const int b = hh >> 1, h = hh & 1;
+                bf16x8 v;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (__bf16)(p[b][8 * h + e] * (dp[b][8 * h + e] - dl[8 * h + e]));
+                sb[b][h] = v;
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          {
+            bf16x8 t[2][2];
+            t[0][0] = fc.col(qtl, qb * 32, 0);
+            t[0][1] = fc.col(qtl, qb * 32 + 16, 0);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              if (db + 1 < DB) {
+                t[(db + 1) & 1][0] = fc.col(qtl, qb * 32, db + 1);
+                t[(db + 1) & 1][1] = fc.col(qtl, qb * 32 + 16, db + 1);
+              }
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                dk[b][db] = mfma32(t[db & 1][0], sb[b][0], dk[b][db]);
+                dk[b][db] = mfma32(t[db & 1][1], sb[b][1], dk[b][db]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        } else {
+          // dS first, then the dV and dK products of each d block together (with the
+          // dQ product's registers, the order above spills in this kernel)
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            dv[b][db] = mfma32(o0, pb[b][0], dv[b][db]);
-            dv[b][db] = mfma32(o1, pb[b][1], dv[b][db]);
-            dk[b][db] = mfma32(t0, sb[b][0], dk[b][db]);
-            dk[b][db] = mfma32(t1, sb[b][1], dk[b][db]);
-          }
-        }
-        // transposed reads (8 per d block) run one d block ahead of their 8 MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            f32x16 ds;
 #pragma unroll
-        for (int db = 0; db < DB - 1; ++db) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            for (int r = 0; r < 16; ++r) ds[r] = p[b][r] * (dp[b][r] - dl[r]);
+            sb[b][0] = pack8(ds, 0);
+            sb[b][1] = pack8(ds, 8);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const bf16x8 o0 = fc.col(dotl, qb * 32, db);
+            const bf16x8 o1 = fc.col(dotl, qb * 32 + 16, db);
+            const bf16x8 t0 = fc.col(qtl, qb * 32, db);
+            const bf16x8 t1 = fc.col(qtl, qb * 32 + 16, db);
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              dv[b][db] = mfma32(o0, pb[b][0], dv[b][db]);
+              dv[b][db] = mfma32(o1, pb[b][1], dv[b][db]);
+              dk[b][db] = mfma32(t0, sb[b][0], dk[b][db]);
+              dk[b][db] = mfma32(t1, sb[b][1], dk[b][db]);
+            }
+          }
+          // transposed reads (8 per d block) run one d block ahead of their 8 MFMAs
           __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int db = 0; db < DB - 1; ++db) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
         if constexpr (ATOMIC) {
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
