@@ -153,6 +153,9 @@ struct DkdvMath {
   // S and dP as vector-register MFMAs (mfma32v_*) where the dK/dV accumulators live in
   // the accumulation registers: workgroups of at most 4 waves (one wave per SIMD)
   static constexpr bool kVgprSP = NW <= 4;
+  // dS between the dV products (one wave per SIMD, 7-GEMM): 1-2% faster at d = 192 and
+  // 256, level or slower at d = 96 (fewer dV products to hide the arithmetic under)
+  static constexpr bool kSplitDS = kVgprSP && !ATOMIC && D >= 192;
 
   __device__ __forceinline__ static void tile(const LDS char* qtl, const LDS char* dotl, const LDS float* stats,
                                               const LDS char* ktile, const LDS char* vtile, LDS char* dst,
@@ -390,38 +393,76 @@ struct DkdvMath {
           }
         }
         f32x16 p, ds;
+        bf16x8 pb0, pb1, sb0, sb1;
+        if constexpr (kSplitDS) {
+          // P first; the dS arithmetic then runs between the dV products (they need only
+          // P), whose results go to the accumulation registers, so the wave overlaps it
+          // with its own MFMAs; the dK products follow
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pv = exp2_hw(fmaf(s[r], c, -l2[r]));
-          p[r] = pv;
-          float dpv = dp[r];
-          if constexpr (DROP) dpv = drop_keep(dr[r >> 3], r & 7, dc.t) ? dpv * ks : 0.f;
-          ds[r] = pv * (dpv - dl[r]);
-        }
-        bf16x8 pb0 = pack8(p, 0), pb1 = pack8(p, 8);
-        if constexpr (DROP) {  // dV takes Pd = P * M * s; s is applied when dV is stored
-          pb0 = drop_mask8(pb0, dr[0], dc.t);
-          pb1 = drop_mask8(pb1, dr[1], dc.t);
-        }
-        bf16x8 sb0 = pack8(ds, 0), sb1 = pack8(ds, 8);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
-          dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
-          dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
-          dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
-          if constexpr (!kReadAhead) fence_every<2>(db);
-        }
-        // transposed reads (8 per d block) run one d block ahead of their 4 MFMAs
-        if constexpr (kReadAhead) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-          for (int db = 0; db < DB - 1; ++db) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+          for (int r = 0; r < 16; ++r) p[r] = exp2_hw(fmaf(s[r], c, -l2[r]));
+          pb0 = pack8(p, 0);
+          pb1 = pack8(p, 8);
+          if constexpr (DROP) {  // dV takes Pd = P * M * s; s is applied when dV is stored
+            pb0 = drop_mask8(pb0, dr[0], dc.t);
+            pb1 = drop_mask8(pb1, dr[1], dc.t);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
+            dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+#pragma unroll
+            for (int r = db * 16 / DB; r < (db + 1) * 16 / DB; ++r) {
+              float dpv = dp[r];
+              if constexpr (DROP) dpv = drop_keep(dr[r >> 3], r & 7, dc.t) ? dpv * ks : 0.f;
+              ds[r] = p[r] * (dpv - dl[r]);
+            }
+            fence_every<1>(db);
+          }
+          sb0 = pack8(ds, 0);
+          sb1 = pack8(ds, 8);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+            fence_every<2>(db);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pv = exp2_hw(fmaf(s[r], c, -l2[r]));
+            p[r] = pv;
+            float dpv = dp[r];
+            if constexpr (DROP) dpv = drop_keep(dr[r >> 3], r & 7, dc.t) ? dpv * ks : 0.f;
+            ds[r] = pv * (dpv - dl[r]);
+          }
+          pb0 = pack8(p, 0);
+          pb1 = pack8(p, 8);
+          if constexpr (DROP) {  // dV takes Pd = P * M * s; s is applied when dV is stored
+            pb0 = drop_mask8(pb0, dr[0], dc.t);
+            pb1 = drop_mask8(pb1, dr[1], dc.t);
+          }
+          sb0 = pack8(ds, 0);
+          sb1 = pack8(ds, 8);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(fc.col(dotl, qb * 32, db), pb0, dv[db]);
+            dv[db] = mfma32(fc.col(dotl, qb * 32 + 16, db), pb1, dv[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32, db), sb0, dk[db]);
+            dk[db] = mfma32(fc.col(qtl, qb * 32 + 16, db), sb1, dk[db]);
+            if constexpr (!kReadAhead) fence_every<2>(db);
+          }
+          // transposed reads (8 per d block) run one d block ahead of their 4 MFMAs
+          if constexpr (kReadAhead) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+            for (int db = 0; db < DB - 1; ++db) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          }
         }
         if constexpr (ATOMIC) {
           if (!CAUSAL && key >= N) {
