@@ -48,3 +48,64 @@ def test_atomic_dq_adds_stay_inside_dq(d, N, causal):
         stray = int(np.count_nonzero(bits != NEG_ZERO_BITS))
         assert stray == 0, "%d elements past the end of dq were written" % stray
         check_backward((dq, dk, dv), refs)
+
+
+# Output tiles staged through LDS: the forward's O, the dQ kernel's dQ and the wide dK/dV
+# kernel's dK and dV leave as whole row segments through buffer stores, whose rows past N
+# must be masked per lane (a first version let the buffer range drop them; the range check
+# does not cover the scalar offset that selects a store's rows, and it wrote into the next
+# head).  Each output sits at the front of a larger buffer whose tail holds a NaN payload
+# no kernel writes; every configuration of each pass must leave that tail untouched.
+SENTINEL_BITS = 0x7FC0DEAD
+
+
+def _tail_buffer(elems, tail=64 * 512):
+    buf = torch.empty(elems + tail, dtype=torch.float32, device="cuda")
+    buf.view(torch.int32).fill_(SENTINEL_BITS)
+    return buf
+
+
+def _tail_intact(buf, elems, what):
+    torch.cuda.synchronize()
+    bits = buf[elems:].view(torch.int32).cpu().numpy()
+    stray = int(np.count_nonzero(bits != SENTINEL_BITS))
+    assert stray == 0, "%s: %d elements past the end were written" % (what, stray)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 256])
+@pytest.mark.parametrize("N", [33, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_output_stores_stay_inside_outputs(d, N, causal):
+    from exact_attention_102_amd import (PASS_DKDV, PASS_DQ, PASS_FWD, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess,
+                                         fa_fwd, fa_num_configs)
+    from parity_util import check_forward, oracle_forward
+    B, H = 1, 2
+    scale = 1.0 / math.sqrt(d)
+    dev, host, _ = make_inputs(B, H, N, d, seed=77 + N + d)
+    q, k, v, do = dev
+    elems = B * H * N * d
+    ro, rl = oracle_forward(host, scale, causal)
+    refs = oracle_backward(host, scale, causal)
+    obuf = _tail_buffer(elems)
+    o = obuf[:elems].view(B, H, N, d)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    for c in range(fa_num_configs(PASS_FWD, d)):
+        note("store bounds fwd d=%d N=%d causal=%d cfg %d" % (d, N, causal, c))
+        fa_fwd(q, k, v, causal, scale, o=o, lse=lse, cfg=c)
+        _tail_intact(obuf, elems, "O, fwd cfg %d" % c)
+        check_forward(o, lse, ro, rl)
+    o, lse = gpu_forward(dev, causal, scale)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    fa_bwd_preprocess(o, do, delta=delta)
+    kbuf, vbuf, qbuf = _tail_buffer(elems), _tail_buffer(elems), _tail_buffer(elems)
+    dk, dv, dq = (x[:elems].view(B, H, N, d) for x in (kbuf, vbuf, qbuf))
+    for c in range(fa_num_configs(PASS_DKDV, d)):
+        note("store bounds dkdv d=%d N=%d causal=%d cfg %d" % (d, N, causal, c))
+        fa_bwd_dkdv(q, k, v, do, lse, delta, causal, scale, False, dk, dv, cfg=c)
+        _tail_intact(kbuf, elems, "dK, dkdv cfg %d" % c)
+        _tail_intact(vbuf, elems, "dV, dkdv cfg %d" % c)
+    for c in range(fa_num_configs(PASS_DQ, d)):
+        note("store bounds dq d=%d N=%d causal=%d cfg %d" % (d, N, causal, c))
+        fa_bwd_dq(q, k, v, do, lse, delta, causal, scale, dq, cfg=c)
+        _tail_intact(qbuf, elems, "dQ, dq cfg %d" % c)
+    check_backward((dq, dk, dv), refs)
