@@ -6,8 +6,8 @@ One step runs the whole path over every workload's synthetic bf16 inputs (alread
 resident in HBM) -- by default both head-dim-128 workloads of the metric, B4 H16
 N2048 (non-causal and causal) and B2 H16 N8192 (causal): for each workload and
 mask, the forward, the 5-GEMM backward (preprocess with dq zeroing, dK/dV kernel
-with fp32-atomic dQ) and the 7-GEMM backward (preprocess, dK/dV kernel, dQ
-kernel).  Every kernel is bracketed by HIP events on the stream it runs on; W
+with fp32-atomic dQ) and the 7-GEMM backward (dQ kernel computing delta itself,
+then the dK/dV kernel reading it).  Every kernel is bracketed by HIP events on the stream it runs on; W
 untimed steps are followed by exactly K timed steps between two device
 synchronisations.
 
@@ -139,7 +139,7 @@ def cpu_baseline(cases, heads_per_workload=-1):
 
 
 DEFAULT_WORKLOADS = "b4_h16_n2048_d128,b2_h16_n8192_d128_causal"
-KERNELS = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]
+KERNELS = ["fwd", "preprocess5", "dkdv_atomic", "dq", "dkdv"]
 
 
 class Case:
@@ -156,12 +156,13 @@ class Case:
         self.o = torch.empty((B, H, N, d), **f32)
         self.lse = torch.empty((B, H, N), **f32)
         self.delta = torch.empty((B, H, N), **f32)
+        self.delta7 = torch.empty((B, H, N), **f32)
         self.dq5, self.dk5, self.dv5 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
         self.dq7, self.dk7, self.dv7 = (torch.empty((B, H, N, d), **f32) for _ in range(3))
 
     def run(self, stream, ev):
-        """fwd | preprocess5 | dkdv_atomic | preprocess7 | dkdv | dq, events ev[0..6] around them."""
-        from exact_attention_102_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_fwd
+        """fwd | preprocess5 | dkdv_atomic | dq (+ delta) | dkdv, events ev[0..5] around them."""
+        from exact_attention_102_amd import fa_bwd_dkdv, fa_bwd_dq_delta, fa_bwd_preprocess, fa_fwd
         w, c = self.w, self.causal
         if ev:
             ev[0].record(stream)
@@ -175,16 +176,14 @@ class Case:
                     dq=self.dq5, stream=stream)
         if ev:
             ev[3].record(stream)
-        fa_bwd_preprocess(self.o, self.do, delta=self.delta, stream=stream)
+        fa_bwd_dq_delta(self.q, self.k, self.v, self.o, self.do, self.lse, c, w.scale, self.delta7, self.dq7,
+                        stream=stream)
         if ev:
             ev[4].record(stream)
-        fa_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.delta, c, w.scale, False, self.dk7, self.dv7,
+        fa_bwd_dkdv(self.q, self.k, self.v, self.do, self.lse, self.delta7, c, w.scale, False, self.dk7, self.dv7,
                     stream=stream)
         if ev:
             ev[5].record(stream)
-        fa_bwd_dq(self.q, self.k, self.v, self.do, self.lse, self.delta, c, w.scale, self.dq7, stream=stream)
-        if ev:
-            ev[6].record(stream)
 
 
 def main():
@@ -227,7 +226,7 @@ def main():
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
-    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in cases] for _ in range(args.steps)]
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in cases] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -252,7 +251,7 @@ def main():
         p = fl["pairs"]
         t_fwd = dur[(case.key, "fwd")]
         t_b5 = dur[(case.key, "preprocess5")] + dur[(case.key, "dkdv_atomic")]
-        t_b7 = dur[(case.key, "preprocess7")] + dur[(case.key, "dkdv")] + dur[(case.key, "dq")]
+        t_b7 = dur[(case.key, "dq")] + dur[(case.key, "dkdv")]
         total_flops += fl["fwd"] + 2 * fl["bwd_effective"]
         ent = {
             "fwd_tflops": fl["fwd"] / t_fwd / 1e9, "fwd_ms": t_fwd,

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dkdv.restype = i
     L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, i]
     L.fa_bwd_dq.restype = i
+    L.fa_bwd_dq_delta.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, vp, vp, i]
+    L.fa_bwd_dq_delta.restype = i
     L.fa_num_configs.argtypes = [i, i, i]
     L.fa_num_configs.restype = i
     L.fa_config_name.argtypes = [i, i, i, i, cp, sz]
@@ -315,6 +317,22 @@ def fa_bwd_dq(q, k, v, dout, lse, delta, causal: bool, scale: float, dq, stream=
     if st != FA_OK:
         raise FAError(st, "fa_bwd_dq")
     return dq
+
+
+def fa_bwd_dq_delta(q, k, v, o, dout, lse, causal: bool, scale: float, delta, dq, stream=None, cfg: int = -1):
+    """7-GEMM dQ kernel that computes delta itself from o and dout and writes it (for
+    fa_bwd_dkdv, run after it); delta and dq must be allocated by the caller."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    ptr = [_check(q, "q", torch.bfloat16), _check(k, "k", torch.bfloat16, q.shape),
+           _check(v, "v", torch.bfloat16, q.shape), _check(o, "o", torch.float32, q.shape),
+           _check(dout, "dout", torch.bfloat16, q.shape), _check(lse, "lse", torch.float32, (B, H, N))]
+    st = lib().fa_bwd_dq_delta(*ptr, B, H, N, d, int(bool(causal)), float(scale),
+                               _check(delta, "delta", torch.float32, (B, H, N)),
+                               _check(dq, "dq", torch.float32, q.shape), _stream_ptr(stream), int(cfg))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_dq_delta")
+    return delta, dq
 
 
 # --------------------------------------------------------------------------- general entry points

@@ -435,6 +435,32 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   return launched();
 }
 
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const float* o, const void* dout,
+                          const float* lse, int B, int H, int N, int d, int causal, float scale, float* delta,
+                          float* dq, void* stream, int cfg) {
+  if (!o || !aligned16(o)) return FA_ERR_INVALID_ARG;
+  float* outs[1] = {dq};
+  // delta is written here: validated as a row buffer, then kept apart from o and dq
+  const fa_status st = check_bwd_stage(q, k, v, dout, lse, delta, B, H, N, d, scale, outs, 1);
+  if (st != FA_OK) return st;
+  const size_t elems = (size_t)B * H * N * d, rows = (size_t)B * H * N;
+  const Range ro = rng(o, elems * 4), rd = rng(delta, rows * 4);
+  if (overlaps(rd, ro) || overlaps(rd, rng(dq, elems * 4)) || overlaps(rd, rng(lse, rows * 4)) ||
+      overlaps(ro, rng(dq, elems * 4)))
+    return FA_ERR_INVALID_ARG;
+  int n = 0;
+  const BwdConfig* t = bwd_table(3, &n);
+  const int j = nth_for_d(t, n, d, cfg < 0 ? default_index(3, d, causal) : cfg);
+  if (j < 0) return FA_ERR_UNSUPPORTED;
+  const Views vw = contiguous_views(H, N, d);
+  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, nullptr, nullptr, vw);
+  a.o = o;
+  a.vo = vw.o;
+  a.delta_out = delta;
+  if (t[j].launch(a, causal != 0, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_INVALID_ARG;
+  return launched();
+}
+
 }  // extern "C"
 
 namespace {
@@ -488,8 +514,9 @@ fa_status bwd_impl(const void* q, const void* k, const void* v, const float* o, 
 namespace {
 
 // The backward's launches on validated views (kernels built for head dim D, tensors with
-// head dim vw.hd <= D): preprocess into delta (and dq cleared for the atomic variant),
-// dK/dV (with atomic dQ), then the dQ kernel for the 7-GEMM variant.
+// head dim vw.hd <= D).  5-GEMM: preprocess into delta with dq cleared, then dK/dV with
+// atomic dQ.  7-GEMM: the dQ kernel, which computes delta itself and writes it, then the
+// dK/dV kernel reading that delta.
 fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dout,
                      int B, int H, int N, int D, int causal, float scale, fa_bwd_variant variant, float* dq, float* dk,
                      float* dv, float* delta, float* dq_scratch, void* stream, int cfg_dkdv, int cfg_dq,
@@ -520,11 +547,26 @@ fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv, vw);
+  set_drop(a, drop);
+  if (!atomic) {
+    // 7-GEMM: the dQ kernel runs first and computes delta itself (from O and the dO rows
+    // it loads anyway), writing it for the dK/dV kernel; no preprocess launch
+    fa::BwdArgs aq = a;
+    aq.o = o;
+    aq.vo = vw.o;
+    aq.delta_out = delta;
+    if (t3[i3].launch(aq, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
+    const fa_status st = launched();
+    if (st != FA_OK) return st;
+    if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
+    return launched();
+  }
   fa::PreArgs p;
   p.o = o;
   p.dout = static_cast<const __bf16*>(dout);
   p.delta = delta;
-  p.dq = atomic ? dq : nullptr;
+  p.dq = dq;
   p.rows = (int)rows;
   p.H = H;
   p.N = N;
@@ -535,18 +577,11 @@ fa_status bwd_launch(const void* q, const void* k, const void* v, const float* o
   if (fa::launch_preprocess(p, d, s) != 0) return FA_ERR_UNSUPPORTED;
   fa_status st = launched();
   if (st != FA_OK) return st;
-
-  fa::BwdArgs a = bwd_args(q, k, v, dout, lse, delta, B, H, N, scale, dq, dk, dv, vw);
-  set_drop(a, drop);
   if (t1[i1].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
   st = launched();
   if (st != FA_OK) return st;
-  if (atomic) {
-    if (!dq_copy) return FA_OK;
-    fa::launch_scatter_f32(dq_scratch, dq_user, vw_in.dq, B, H, N, vw_in.hd, D, s);
-    return launched();
-  }
-  if (t3[i3].launch(a, causal != 0, s) != 0) return FA_ERR_INVALID_ARG;
+  if (!dq_copy) return FA_OK;
+  fa::launch_scatter_f32(dq_scratch, dq_user, vw_in.dq, B, H, N, vw_in.hd, D, s);
   return launched();
 }
 

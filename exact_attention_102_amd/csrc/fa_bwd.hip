@@ -1311,7 +1311,31 @@ __global__ __launch_bounds__(NW * 64, OCC) void dq_kernel(BwdArgs a) {
     dof[kk] = load_row_chunk(dOh + (size_t)qrow * a.vdo.sn, 2 * kk + g, hd >> 3);
   }
   const float lse2 = qi < N ? a.lse[(size_t)bh * N + qi] * kLog2e : INFINITY;
-  const float dl = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  float dl;
+  if (a.o) {
+    // delta of the lane's row, sum_k dO_ik O_ik, from the dO chunks already in registers
+    // (lane half g holds columns 16 kk + 8 g .. + 7) and the same columns of O
+    const float* orow = a.o + head_base(a.vo, bh, a.H) + (size_t)qrow * a.vo.sn;
+    float acc = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int ch = 2 * kk + g;
+      if (ch < (hd >> 3)) {
+        const f32x4 o0 = *(const f32x4*)(orow + 8 * ch);
+        const f32x4 o1 = *(const f32x4*)(orow + 8 * ch + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf((float)dof[kk][e], o0[e], acc);
+          acc = fmaf((float)dof[kk][4 + e], o1[e], acc);
+        }
+      }
+    }
+    acc = half_swap_sum(acc);
+    dl = qi < N ? acc : 0.f;
+    if (g == 0 && qi < N) a.delta_out[(size_t)bh * N + qi] = acc;
+  } else {
+    dl = qi < N ? a.delta[(size_t)bh * N + qi] : 0.f;
+  }
   f32x16 dq[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = zero16();

@@ -51,6 +51,11 @@ struct BwdArgs {
   float drop_scale = 1.f;
   View vq{}, vk{}, vv{}, vdo{}, vdq{}, vdk{}, vdv{};  // vdo.sn == vq.sn (one tile copier serves both)
   int hd = 0;
+  // dQ kernel only: with o set, it computes delta itself from O and dO (no preprocess
+  // launch) and writes it to delta_out for the dK/dV kernel that runs after it
+  const float* o = nullptr;
+  View vo{};
+  float* delta_out = nullptr;
 };
 
 struct PreArgs {

@@ -68,7 +68,7 @@ def stats_table(prof_dir: str) -> str:
     return "\n".join(out)
 
 
-KERNEL_ORDER = ["fwd", "preprocess5", "dkdv_atomic", "preprocess7", "dkdv", "dq"]   # bench.py's step order
+KERNEL_ORDER = ["fwd", "preprocess5", "dkdv_atomic", "dq", "dkdv"]   # bench.py's step order
 
 
 def trace_table(prof_dir: str, bench_json: str, steps: int, warmup: int) -> str:

@@ -9,7 +9,7 @@ benchmark snippet in "Potential algorithmic improvements for backward pass"
 
 * the forward;
 * the 5-GEMM backward: preprocess (delta, dq cleared) + dK/dV with atomic dQ;
-* the 7-GEMM backward: preprocess + dK/dV + dQ kernel.
+* the 7-GEMM backward: dQ kernel (computing delta) + dK/dV.
 
 Throughput is credited with 4 d flop per unmasked pair (forward) and 10 d per pair
 (both backward designs, the 5-GEMM count, as that page compares them); the 7-GEMM
@@ -65,7 +65,7 @@ def main():
     import torch
 
     import workloads
-    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_config_name,
+    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq_delta, fa_bwd_preprocess, fa_config_name,
                                          fa_default_config, fa_fwd, lib)
     from exact_attention_102_amd.flops import attention_flops, mfa_op_counts
     from exact_attention_102_amd.sweep import time_calls
@@ -92,9 +92,8 @@ def main():
             fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, True, dk, dv, dq=dq)
 
         def bwd7():
-            fa_bwd_preprocess(o, do, delta=delta)
+            fa_bwd_dq_delta(q, k, v, o, do, lse, causal, w.scale, delta, dq)
             fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, False, dk, dv)
-            fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq)
 
         fwd()
         torch.cuda.synchronize()

@@ -51,7 +51,7 @@ def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3), d_override: 
     import torch
 
     import workloads
-    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_config_name,
+    from exact_attention_102_amd import (fa_bwd_dkdv, fa_bwd_dq_delta, fa_bwd_preprocess, fa_config_name,
                                          fa_default_config, fa_fwd, fa_num_configs)
     from exact_attention_102_amd.flops import attention_flops
 
@@ -80,7 +80,7 @@ def sweep(workload: str, causal_override=None, passes=(0, 1, 2, 3), d_override: 
                 atomic = pass_id == 2
                 fn = lambda: fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, atomic, dk, dv, dq=dq, cfg=cfg)
             else:
-                fn = lambda: fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq, cfg=cfg)
+                fn = lambda: fa_bwd_dq_delta(q, k, v, o, do, lse, causal, w.scale, delta, dq, cfg=cfg)
             best, med = time_calls(fn, torch)
             flops = 2 * gemms[pass_id] * d * p
             rec = {"workload": w.name, "causal": causal, "pass": ["fwd", "dkdv", "dkdv_atomic", "dq"][pass_id],

@@ -52,7 +52,7 @@ def run(workload: str):
     import torch
 
     import workloads
-    from exact_attention_102_amd import fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess, fa_fwd
+    from exact_attention_102_amd import fa_bwd_dkdv, fa_bwd_dq_delta, fa_bwd_preprocess, fa_fwd
 
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
@@ -72,8 +72,8 @@ def run(workload: str):
         fa_fwd(q, k, v, causal, w.scale, o=o, lse=lse)
         fa_bwd_preprocess(o, do, delta=delta, dq=dq)
         fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, True, dk, dv, dq=dq)
+        fa_bwd_dq_delta(q, k, v, o, do, lse, causal, w.scale, delta, dq)
         fa_bwd_dkdv(q, k, v, do, lse, delta, causal, w.scale, False, dk, dv)
-        fa_bwd_dq(q, k, v, do, lse, delta, causal, w.scale, dq)
         torch.cuda.synchronize()
     print("traffic run done", flush=True)
 

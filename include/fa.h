@@ -118,8 +118,10 @@ fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const floa
 fa_status fa_bwd_preprocess(const float* o, const void* dout, int B, int H, int N, int d, float* delta,
                             float* dq, int zero_dq, void* stream);
 
-/* The backward's two kernel stages on their own (fa_bwd runs preprocess, then
- * these).  delta must hold the preprocess result for the same o/dout.
+/* The backward's kernel stages on their own.  fa_bwd runs, for the 5-GEMM design,
+ * fa_bwd_preprocess (with zero_dq) and then fa_bwd_dkdv with atomic_dq; for the 7-GEMM
+ * design, fa_bwd_dq_delta and then fa_bwd_dkdv.  For fa_bwd_dkdv and fa_bwd_dq, delta
+ * must hold the preprocess result for the same o/dout.
  * fa_bwd_dkdv: dk, dv (fp32 [B,H,N,d], written).  With atomic_dq != 0 it also adds
  *   scale * dS K into dq with fp32 atomics (the 5-GEMM design; dq must already be
  *   zero or hold a partial sum); with atomic_dq == 0, dq is ignored (may be NULL).
@@ -132,6 +134,18 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
 fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                     const float* delta, int B, int H, int N, int d, int causal, float scale, float* dq,
                     void* stream, int cfg);
+
+/* The 7-GEMM design's first backward launch: the dQ kernel computing each row's delta
+ * itself (the preprocess's sum_k dout_ik * o_ik, from the dO rows the kernel loads for
+ * its own products and the same columns of o) instead of reading it, and writing it to
+ * delta for fa_bwd_dkdv, which runs after it -- one launch and one pass over O and dO
+ * fewer than preprocess + dQ.
+ *   o : fp32 [B,H,N,d] (read), delta : fp32 [B,H,N] (written), dq : fp32 [B,H,N,d]
+ *   (written once per element); delta must overlap neither o, dq nor lse.
+ * Errors as fa_bwd_dq; cfg: tile configuration of pass 3 (-1 = default). */
+fa_status fa_bwd_dq_delta(const void* q, const void* k, const void* v, const float* o, const void* dout,
+                          const float* lse, int B, int H, int N, int d, int causal, float scale, float* delta,
+                          float* dq, void* stream, int cfg);
 
 /* Tile configurations, for the block-shape sweep ("Potential algorithmic
  * improvements for backward pass": search over block dimensions under register

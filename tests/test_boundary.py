@@ -119,6 +119,18 @@ def test_bwd_rejects_bad_arguments(L):
                                None) == FA_ERR_INVALID_ARG
     assert L.fa_bwd_preprocess(ctypes.c_void_p(P), ctypes.c_void_p(P + MB), 1, 1, 8, 64, ctypes.c_void_p(P + 2 * MB),
                                None, 1, None) == FA_ERR_INVALID_ARG   # zero_dq without dq
+    # the fused dQ stage: o is required, and the delta it writes may alias neither o nor dq
+    ptrs = [ctypes.c_void_p(P + i * MB) for i in range(4)]   # q k v dout
+    lse = ctypes.c_void_p(P + 4 * MB)
+
+    def dqd(o, delta, dq):
+        return L.fa_bwd_dq_delta(*ptrs[:3], o, ptrs[3], lse, 1, 1, 8, 64, 0, 0.125, delta, dq, None, -1)
+    o, delta, dq = ctypes.c_void_p(P + 5 * MB), ctypes.c_void_p(P + 6 * MB), ctypes.c_void_p(P + 7 * MB)
+    assert dqd(None, delta, dq) == FA_ERR_INVALID_ARG
+    assert dqd(o, o, dq) == FA_ERR_INVALID_ARG               # delta aliases o
+    assert dqd(o, dq, dq) == FA_ERR_INVALID_ARG              # delta aliases dq
+    assert dqd(o, delta, o) == FA_ERR_INVALID_ARG            # dq aliases o
+    assert dqd(o, delta, ctypes.c_void_p(P)) == FA_ERR_INVALID_ARG   # dq aliases q
 
 
 def test_heads_of_2gib_or_more_rejected(L):

@@ -76,7 +76,7 @@ def _tail_intact(buf, elems, what):
 @pytest.mark.parametrize("N", [33, 300])
 @pytest.mark.parametrize("causal", [False, True])
 def test_output_stores_stay_inside_outputs(d, N, causal):
-    from exact_attention_102_amd import (PASS_DKDV, PASS_DQ, PASS_FWD, fa_bwd_dkdv, fa_bwd_dq, fa_bwd_preprocess,
+    from exact_attention_102_amd import (PASS_DKDV, PASS_DQ, PASS_FWD, fa_bwd_dkdv, fa_bwd_dq_delta, fa_bwd_preprocess,
                                          fa_fwd, fa_num_configs)
     from parity_util import check_forward, oracle_forward
     B, H = 1, 2
@@ -104,8 +104,14 @@ def test_output_stores_stay_inside_outputs(d, N, causal):
         fa_bwd_dkdv(q, k, v, do, lse, delta, causal, scale, False, dk, dv, cfg=c)
         _tail_intact(kbuf, elems, "dK, dkdv cfg %d" % c)
         _tail_intact(vbuf, elems, "dV, dkdv cfg %d" % c)
+    rows = B * H * N
+    dbuf = _tail_buffer(rows)
+    delta7 = dbuf[:rows].view(B, H, N)
     for c in range(fa_num_configs(PASS_DQ, d)):
         note("store bounds dq d=%d N=%d causal=%d cfg %d" % (d, N, causal, c))
-        fa_bwd_dq(q, k, v, do, lse, delta, causal, scale, dq, cfg=c)
+        fa_bwd_dq_delta(q, k, v, o, do, lse, causal, scale, delta7, dq, cfg=c)
         _tail_intact(qbuf, elems, "dQ, dq cfg %d" % c)
+        _tail_intact(dbuf, rows, "delta, dq cfg %d" % c)
+        # the delta the dQ kernel computes is the preprocess's up to fp32 summation order
+        assert torch.allclose(delta7, delta, rtol=1e-5, atol=1e-5), (delta7 - delta).abs().max().item()
     check_backward((dq, dk, dv), refs)
