@@ -92,9 +92,8 @@ int default_index(int pass, int d, int causal) {
   switch (pass) {
     case 0:  // fwd (opt = optimistic statistics): d64 Br32x4 Bc64 three waves per SIMD opt (causal: Br32x8
              // Bc64 exact, which the sharp causal workload needs), d96 Br32x8 Bc64 opt (causal: Br32x4 Bc32
-             // three waves per SIMD opt), d128 Br32x4 Bc64 two waves per SIMD opt (causal: Bc32 three opt),
-             // d192 and d256 Bc32 opt
-      if (d == 128) return causal ? 5 : 6;
+             // three waves per SIMD opt), d128 Br32x8 Bc64 opt (both masks), d192 and d256 Bc32 opt
+      if (d == 128) return 11;
       if (d == 256) return 2;
       if (d == 96) return causal ? 3 : 4;
       if (d == 192) return 3;

@@ -604,6 +604,8 @@ const FwdConfig* fwd_configs(int* count) {
       // head dims above 256 on 384-wide tiles
       FWD_CFGVO(384, 288, 32, 4, 1), FWD_CFGVO(384, 320, 32, 4, 1), FWD_CFGVO(384, 352, 32, 4, 1),
       FWD_CFGVO(384, 384, 32, 4, 1),
+      // eight waves over 256 query rows: each K/V tile copied once for twice the rows
+      FWD_CFGO(128, 64, 8, 2),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
