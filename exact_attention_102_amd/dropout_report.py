@@ -86,8 +86,9 @@ def main():
     if args.out:
         with open(args.out, "w") as fh:
             fh.write("# Fused dropout on P: cost per pass (one MI355X), p = %g\n\n" % p)
+            # the command as run from the repository root, writing the committed file
             fh.write("Command (from the repository root): `python -m exact_attention_102_amd.dropout_report --out "
-                     "%s`\n\n" % args.out)
+                     "profiles/%s`\n\n" % os.path.basename(args.out))
             fh.write("Best of 5 trials x 5 dispatches.  TFLOP/s credit the undropped attention (4d fwd, 10d bwd "
                      "flop per unmasked pair; peak 2500).  Slowdown = time with dropout / time without.\n\n")
             fh.write("| workload | mask | fwd TF | fwd+drop TF | x | 5-GEMM TF | +drop TF | x | 7-GEMM TF | +drop TF | x "

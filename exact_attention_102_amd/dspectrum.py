@@ -105,8 +105,9 @@ def main():
     if args.out:
         with open(args.out, "w") as fh:
             fh.write("# Head-dimension spectrum (one MI355X), B%d H%d N%d, non-causal\n\n" % (B, H, N))
-            fh.write("Command (from the repository root): `python -m exact_attention_102_amd.dspectrum --out %s`\n\n"
-                     % args.out)
+            # the command as run from the repository root, writing the committed file
+            fh.write("Command (from the repository root): `python -m exact_attention_102_amd.dspectrum --out "
+                     "profiles/%s`\n\n" % os.path.basename(args.out))
             fh.write("Best of 5 trials x 5 dispatches.  TFLOP/s credit the true head dim D: 4D (fwd) and 10D (both "
                      "backward designs) flop per pair, peak 2500.  G instr/s: the page's (2D+5) N^2 for the forward "
                      "and (3D+5) N^2 + (4D+5) N^2 for the 7-GEMM backward's two kernels.  Head dims other than "

@@ -140,6 +140,15 @@ def main():
                 fh.write(json.dumps(r) + "\n")
     if args.md:
         with open(args.md, "w") as fh:
+            # the command as run from the repository root, writing the committed file
+            cmd = "python -m exact_attention_102_amd.sweep " + (
+                "--all" if args.all else "--workload %s --causal %d --passes %s%s" % (
+                    args.workload, args.causal, args.passes, " --d %d" % args.d if args.d else ""))
+            fh.write("# Block-shape sweep: every configuration of each pass (one MI355X)\n\n"
+                     "Command (from the repository root): `%s --md profiles/%s`\n\n"
+                     "Best and median of 5 trials x 5 dispatches; `default` marks the configuration the "
+                     "library picks for that head dim and mask; `vs fastest` = best time / fastest best "
+                     "time in the table.\n" % (cmd, os.path.basename(args.md)))
             fh.write(markdown(recs) + "\n")
 
 
