@@ -613,7 +613,7 @@ const FwdConfig* fwd_configs(int* count) {
 
 const FwdConfig* fwd_dropout_configs(int* count) {
   static const FwdConfig table[] = {
-      FWD_DROP_CFG(64, 64, 64, 8, 2),   FWD_DROP_CFG(128, 128, 64, 4, 2), FWD_DROP_CFG(256, 256, 32, 4, 1),
+      FWD_DROP_CFG(64, 64, 64, 8, 2),   FWD_DROP_CFG(128, 128, 64, 8, 2), FWD_DROP_CFG(256, 256, 32, 4, 1),
       FWD_DROP_CFG(128, 96, 64, 4, 2),  FWD_DROP_CFG(256, 192, 32, 4, 1),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
